@@ -1,0 +1,121 @@
+/*
+ * libssd -- Mamba-2 SSD selective state-space scan, forward pass, on one
+ * MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ types, no
+ * exceptions across the boundary.
+ *
+ * What it computes ("Mamba-2架构与LaCT并行计算技术解析", §1.1 state update):
+ * for every sequence and head, in processing order t,
+ *     d_t = softplus(d_raw_t + d_init)
+ *     H_t = exp(-d_t) * H_{t-1} + d_t * B_t^T X_t        (H: d_state x headdim)
+ *     y_t = C_t H_t
+ * with independent heads (§1.2 of the same page), H_{-1} = init_state (zeros
+ * when NULL), and final_state = H after the sequence's last processed token.
+ * The scan is evaluated in the chunked semiseparable form of
+ * "长序列 Mamba 多卡训练，算力和显存怎么同时省", §一 (a dense diagonal block per
+ * chunk plus a small state handed between chunks), with the state handed on
+ * as (decay, state) pairs as in the Mamba context-parallel scheme of
+ * "揭秘MindSpeed-LLM多潜在注意力（MLA）与Mamba上下文并行实现原理", §三.2.
+ *
+ * Packed variable-length batches (cu_seqlens) follow §三 of the qwbw.cn page
+ * above: each segment [cu[i], cu[i+1]) is an independent sequence whose
+ * state starts from init_state[i].  reverse != 0 runs every sequence from
+ * its last token to its first (the flipped pass of the bidirectional mode,
+ * jsqmd.com page §3.1) and writes y at each token's own position, so no
+ * flipped copy of any tensor is made.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates no device
+ * memory, does not synchronize the stream, and keeps no mutable global
+ * state; calls on different streams with separate workspaces may run
+ * concurrently.  All argument checks run on the host before any launch; on
+ * an error status nothing is launched and no output is written.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* Status codes: 0 is success, every error is negative. */
+enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = -1,        /* a required pointer is NULL                 */
+    SSD_ERR_SHAPE = -2,           /* inconsistent or out-of-range sizes         */
+    SSD_ERR_DTYPE = -3,           /* unknown dtype code                          */
+    SSD_ERR_ALIGN = -4,           /* pointer or stride not 16-byte aligned       */
+    SSD_ERR_UNSUPPORTED = -5,     /* valid but not built (chunk_size, d_state..) */
+    SSD_ERR_WORKSPACE = -6,       /* workspace NULL or smaller than required     */
+    SSD_ERR_HIP = -7,             /* a HIP launch or runtime call failed         */
+    SSD_ERR_CU_SEQLENS = -8       /* cu_seqlens invalid (checked only when the
+                                     environment sets SSD_CHECK=1)               */
+};
+
+/* Element type of x, d_raw, B, C and y.  States are always float32. */
+enum { SSD_F32 = 0, SSD_BF16 = 1 };
+
+/* Problem sizes.  Tokens are laid out [batch][seqlen]; with cu_seqlens the
+ * batch must be 1 and seqlen is the total packed length. */
+typedef struct ssd_dims {
+    int32_t batch;       /* b >= 1                                             */
+    int64_t seqlen;      /* L >= 0 tokens per batch row                        */
+    int32_t nheads;      /* H >= 1                                             */
+    int32_t headdim;     /* P: multiple of 16, 16..512                         */
+    int32_t d_state;     /* N: 16, 32, 64, 128 or 256 (bf16); up to 128 (f32) */
+    int32_t ngroups;     /* G >= 1, divides H; head h reads group h*G/H        */
+    int32_t chunk_size;  /* must be 64                                         */
+    int32_t nseq;        /* number of cu_seqlens segments (0 without them)     */
+    int32_t dtype;       /* SSD_F32 or SSD_BF16                                */
+} ssd_dims;
+
+/* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */
+int ssd_abi_version(void);
+
+/* Bytes of device workspace ssd_fwd needs for these sizes (0 when the sizes
+ * are invalid).  The value depends only on *dims, never on data. */
+size_t ssd_fwd_workspace_bytes(const ssd_dims* dims);
+
+/*
+ * Forward scan.  Device pointers, all row-major and contiguous except y:
+ *   x           [b, L, H, P]   dtype
+ *   d_raw       [b, L, H]      dtype
+ *   d_init      scalar added to d_raw before softplus
+ *   B, C        [b, L, G, N]   dtype
+ *   init_state  [S, H, N, P]   float32, or NULL for zeros
+ *   cu_seqlens  [nseq + 1]     int32 on the device, or NULL; must start at 0,
+ *               be non-decreasing and end at L (only checked when SSD_CHECK=1;
+ *               other values are clamped into range so no access leaves the
+ *               buffers, but the result is then unspecified)
+ *   reverse     0 = causal, 1 = anti-causal within each sequence
+ *   y           output [b, L, H, P] of dtype, element (bi, l, h, p) at
+ *               y + (bi*L + l)*y_token_stride + h*y_head_stride + p;
+ *               strides in elements, multiples of 16 bytes
+ *   final_state output [S, H, N, P] float32, or NULL to skip
+ *   workspace   device scratch of at least ssd_fwd_workspace_bytes(dims)
+ *               bytes, 256-byte aligned; contents need no initialisation
+ *   stream      hipStream_t to launch on (NULL = default stream)
+ * S is b without cu_seqlens and nseq with them.  x, B, C and y must be
+ * 16-byte aligned; they may be NULL only when b*L == 0.  Returns SSD_OK once
+ * the work is queued on the stream.
+ */
+int ssd_fwd(const ssd_dims* dims,
+            const void* x, const void* d_raw, float d_init,
+            const void* B, const void* C,
+            const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+            void* y, int64_t y_token_stride, int64_t y_head_stride,
+            float* final_state,
+            void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* ssd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

@@ -1,0 +1,11 @@
+"""MI355X-native Mamba-2 SSD chunked scan (forward).
+
+The compute runs in ``libssd.so`` (HIP kernels for gfx950 behind the C ABI
+of ``include/ssd.h``); this package is its Python binding.  Functions carry
+the C names: ``ssd_fwd``, ``ssd_fwd_workspace_bytes``, ``ssd_status_string``,
+``ssd_abi_version``; ``ssd_fwd_bidir`` is the forward + reverse helper.
+"""
+from ._binding import (  # noqa: F401
+    CHUNK, SSD_BF16, SSD_F32, SsdDims, SsdError, dims_for, library, make_dims,
+    ssd_abi_version, ssd_fwd, ssd_fwd_bidir, ssd_fwd_workspace_bytes, ssd_status_string,
+)

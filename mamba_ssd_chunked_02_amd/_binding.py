@@ -1,0 +1,189 @@
+"""ctypes binding of libssd (include/ssd.h): argument marshalling only.
+
+Every step of the scan runs in the HIP library; this module maps torch
+tensors to pointers and sizes, allocates outputs and workspace with torch,
+and passes torch's current HIP stream.  If libssd.so is missing the import
+of the library raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+SSD_F32 = 0
+SSD_BF16 = 1
+CHUNK = 64
+
+_DTYPES = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+
+
+class SsdDims(ctypes.Structure):
+    """Mirror of ``ssd_dims`` in include/ssd.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int32),
+        ("headdim", ctypes.c_int32),
+        ("d_state", ctypes.c_int32),
+        ("ngroups", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("nseq", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, where: str = "ssd_fwd"):
+        self.status = status
+        super().__init__(f"{where} returned {status}: {ssd_status_string(status)}")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libssd.so (built by ``mamba_ssd_chunked_02_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} not found: build it with `python -m mamba_ssd_chunked_02_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ssd_abi_version.restype = ctypes.c_int
+        lib.ssd_abi_version.argtypes = []
+        lib.ssd_fwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_fwd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims)]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_fwd.restype = ctypes.c_int
+        lib.ssd_fwd.argtypes = [
+            ctypes.POINTER(SsdDims),
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p,
+        ]
+        _lib = lib
+    return _lib
+
+
+def ssd_abi_version() -> int:
+    return int(library().ssd_abi_version())
+
+
+def ssd_status_string(status: int) -> str:
+    return library().ssd_status_string(int(status)).decode()
+
+
+def make_dims(batch, seqlen, nheads, headdim, d_state, ngroups=1, chunk_size=CHUNK,
+              nseq=0, dtype=SSD_BF16) -> SsdDims:
+    return SsdDims(int(batch), int(seqlen), int(nheads), int(headdim), int(d_state),
+                   int(ngroups), int(chunk_size), int(nseq), int(dtype))
+
+
+def ssd_fwd_workspace_bytes(dims: SsdDims) -> int:
+    return int(library().ssd_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def dims_for(x, B, chunk_size=CHUNK, cu_seqlens=None) -> SsdDims:
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    return make_dims(b, L, H, P, N, G, chunk_size, nseq, _DTYPES[x.dtype])
+
+
+def ssd_fwd(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlens=None,
+            reverse=False, y=None, final_state=True, workspace=None):
+    """Run the SSD forward scan on the GPU.
+
+    x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] (bf16 or fp32, one dtype, on
+    one GPU, contiguous); init_state [S,H,N,P] fp32 or None; cu_seqlens
+    [nseq+1] int32 (b must be 1) or None.  ``y`` may be a preallocated
+    [b,L,H,P] tensor or strided view (last dim contiguous).  Pass
+    ``final_state=False`` to skip it or a [S,H,N,P] fp32 tensor to fill.
+    Returns (y, final_state or None).  Launches on torch's current stream.
+    """
+    if x.dim() != 4 or d_raw.dim() != 3 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] expected")
+    b, L, H, P = x.shape
+    dev = x.device
+    for name, t in (("d_raw", d_raw), ("B", B), ("C", C)):
+        if t.device != dev or t.dtype != x.dtype:
+            raise ValueError(f"{name} must be on {dev} with dtype {x.dtype}")
+    if tuple(d_raw.shape) != (b, L, H) or tuple(B.shape[:2]) != (b, L) or B.shape != C.shape:
+        raise ValueError("shape mismatch between x, d_raw, B and C")
+    for name, t in (("x", x), ("d_raw", d_raw), ("B", B), ("C", C)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    G, N = B.shape[2], B.shape[3]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the same device")
+        cu_seqlens = cu_seqlens.contiguous()
+    S = (cu_seqlens.numel() - 1) if cu_seqlens is not None else b
+    if init_state is not None:
+        if init_state.dtype != torch.float32 or tuple(init_state.shape) != (S, H, N, P) \
+                or init_state.device != dev:
+            raise ValueError(f"init_state must be float32 [{S},{H},{N},{P}] on {dev}")
+        init_state = init_state.contiguous()
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        if tuple(y.shape) != (b, L, H, P) or y.dtype != x.dtype or y.device != dev:
+            raise ValueError("y must match x in shape, dtype and device")
+        if y.stride(3) != 1 or (b > 1 and y.stride(0) != L * y.stride(1)):
+            raise ValueError("y needs a contiguous last dim and batch stride L*token stride")
+    if final_state is True:
+        final_state = torch.empty((S, H, N, P), dtype=torch.float32, device=dev)
+    elif final_state is False or final_state is None:
+        final_state = None
+    elif tuple(final_state.shape) != (S, H, N, P) or final_state.dtype != torch.float32 \
+            or not final_state.is_contiguous():
+        raise ValueError(f"final_state must be contiguous float32 [{S},{H},{N},{P}]")
+    dims = dims_for(x, B, chunk_size, cu_seqlens)
+    need = ssd_fwd_workspace_bytes(dims)  # 0 for invalid sizes: ssd_fwd reports why
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = library().ssd_fwd(
+            ctypes.byref(dims), _ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
+            _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0,
+            _ptr(y), y.stride(1), y.stride(2), _ptr(final_state),
+            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SsdError(rc)
+    return y, final_state
+
+
+def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,
+                  cu_seqlens=None, final_state=False, workspace=None):
+    """Bidirectional scan: a forward pass and a reverse pass over the same
+    inputs, outputs concatenated on the last dim -> y [b,L,H,2P].  The
+    reverse pass runs each sequence from its end to its start and writes at
+    each token's own position, so no flipped copies are made.
+    Returns (y, (final_fwd, final_rev) or None)."""
+    b, L, H, P = x.shape
+    y = torch.empty((b, L, H, 2 * P), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        need = ssd_fwd_workspace_bytes(dims_for(x, B, chunk_size, cu_seqlens))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _, ff = ssd_fwd(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, False,
+                    y=y[..., :P], final_state=final_state, workspace=workspace)
+    _, fr = ssd_fwd(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, True,
+                    y=y[..., P:], final_state=final_state, workspace=workspace)
+    return y, ((ff, fr) if final_state else None)

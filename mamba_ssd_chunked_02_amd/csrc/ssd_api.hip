@@ -1,0 +1,212 @@
+// C ABI of libssd: argument checks, planning and the launch sequence.
+// Every check runs on the host before anything is launched.
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/ssd.h"
+#include "ssd_internal.h"
+
+namespace {
+
+using ssd::kChunk;
+using ssd::kPGroup;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+    int32_t K = 1;          // chunks per span
+    int32_t sps = 0;        // spans per sequence (batch mode)
+    int32_t npg = 0;        // headdim column groups
+    int64_t nspan = 0;      // span slots
+    size_t off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
+    size_t total = 0;
+};
+
+// Chunks per span: the state stays on chip inside a span and only span
+// borders go through HBM, so longer spans move fewer bytes; but each span is
+// walked by one workgroup, so spans are kept short enough that the grid
+// still holds >= 2048 workgroups (8 per CU).  SSD_SPAN_CHUNKS overrides it.
+int32_t choose_k(int64_t chunk_units) {
+    if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 64) return v;
+    }
+    int32_t K = 1;
+    while (K < 8 && chunk_units / (2 * K) >= 2048) K *= 2;
+    return K;
+}
+
+int make_plan(const ssd_dims* d, Plan* pl) {
+    if (!d) return SSD_ERR_NULL_ARG;
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (d->batch < 1 || d->seqlen < 0 || d->nheads < 1 || d->ngroups < 1 || d->nseq < 0)
+        return SSD_ERR_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
+    if (d->headdim < 16 || d->headdim % 16 != 0 || d->headdim > 512) return SSD_ERR_SHAPE;
+    if (d->d_state < 1 || d->d_state > 4096) return SSD_ERR_SHAPE;
+    if (d->chunk_size != kChunk) return SSD_ERR_UNSUPPORTED;
+    if (ssd::span_lds_bytes(d->dtype, d->d_state, true) == 0) return SSD_ERR_UNSUPPORTED;
+    if (d->nseq > 0 && d->batch != 1) return SSD_ERR_SHAPE;
+    const int64_t T = (int64_t)d->batch * d->seqlen;
+    if (d->nseq > 0 && T > INT32_MAX) return SSD_ERR_SHAPE;
+    if (T > ((int64_t)1 << 40)) return SSD_ERR_SHAPE;
+
+    pl->npg = (int32_t)ceil_div(d->headdim, kPGroup);
+    const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
+                                          : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);
+    pl->K = choose_k(nch_bound * d->nheads * pl->npg);
+    if (d->nseq > 0) {
+        pl->sps = 0;
+        pl->nspan = ceil_div(T, (int64_t)kChunk * pl->K) + d->nseq;
+    } else {
+        pl->sps = (int32_t)ceil_div(ceil_div(d->seqlen, kChunk), pl->K);
+        pl->nspan = (int64_t)d->batch * pl->sps;
+    }
+    size_t off = 0;
+    pl->off_states = off;
+    off = align_up(off + (size_t)pl->nspan * d->nheads * d->headdim * d->d_state * sizeof(float));
+    pl->off_decay = off;
+    off = align_up(off + (size_t)pl->nspan * d->nheads * sizeof(float));
+    if (d->nseq > 0) {
+        pl->off_cu = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        pl->off_spoff = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        pl->off_table = off;
+        off = align_up(off + (size_t)pl->nspan * sizeof(int4));
+    }
+    pl->total = off;
+    return SSD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// SSD_CHECK=1: copy cu_seqlens to the host (synchronizes the stream) and
+// check 0 = cu[0] <= cu[1] <= ... <= cu[nseq] = L.
+int check_cu(const int32_t* cu, int32_t nseq, int64_t T, hipStream_t s) {
+    std::vector<int32_t> h(nseq + 1);
+    if (hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * (nseq + 1), hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return SSD_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SSD_ERR_HIP;
+    if (h[0] != 0 || h[nseq] != T) return SSD_ERR_CU_SEQLENS;
+    for (int32_t i = 0; i < nseq; ++i)
+        if (h[i + 1] < h[i]) return SSD_ERR_CU_SEQLENS;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+size_t ssd_fwd_workspace_bytes(const ssd_dims* dims) {
+    Plan pl;
+    if (make_plan(dims, &pl) != SSD_OK) return 0;
+    return pl.total;
+}
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK: success";
+        case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG: a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: inconsistent or out-of-range sizes or strides";
+        case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype code";
+        case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer or stride not 16-byte aligned";
+        case SSD_ERR_UNSUPPORTED:
+            return "SSD_ERR_UNSUPPORTED: chunk_size or d_state not built into this library";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call or kernel launch failed";
+        case SSD_ERR_CU_SEQLENS:
+            return "SSD_ERR_CU_SEQLENS: cu_seqlens not 0..L and non-decreasing";
+    }
+    return "unknown ssd status";
+}
+
+int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init, const void* B,
+            const void* C, const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+            void* y, int64_t y_token_stride, int64_t y_head_stride, float* final_state,
+            void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    const int st = make_plan(dims, &pl);
+    if (st != SSD_OK) return st;
+    const ssd_dims& d = *dims;
+    const int64_t T = (int64_t)d.batch * d.seqlen;
+    if (T > 0 && (!x || !d_raw || !B || !C || !y)) return SSD_ERR_NULL_ARG;
+    if (d.nseq > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
+    if (d.nseq == 0 && cu_seqlens) return SSD_ERR_SHAPE;
+    if (reverse != 0 && reverse != 1) return SSD_ERR_SHAPE;
+    const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
+    const int64_t per_unit = 16 / esz;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y)) return SSD_ERR_ALIGN;
+    if (y_token_stride % per_unit != 0 || y_head_stride % per_unit != 0) return SSD_ERR_ALIGN;
+    if (y_token_stride < 0 || y_head_stride < 0) return SSD_ERR_SHAPE;
+    if (((uintptr_t)init_state & 3u) || ((uintptr_t)final_state & 3u)) return SSD_ERR_ALIGN;
+    if (pl.total > 0) {
+        if (!workspace || workspace_bytes < pl.total) return SSD_ERR_WORKSPACE;
+        if ((uintptr_t)workspace % kAlign) return SSD_ERR_ALIGN;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (d.nseq > 0) {
+        const char* chk = getenv("SSD_CHECK");
+        if (chk && chk[0] == '1') {
+            const int c = check_cu(cu_seqlens, d.nseq, T, s);
+            if (c != SSD_OK) return c;
+        }
+    }
+
+    char* ws = (char*)workspace;
+    ssd::KParams p;
+    memset(&p, 0, sizeof(p));
+    p.x = x;
+    p.d_raw = d_raw;
+    p.B = B;
+    p.C = C;
+    p.y = y;
+    p.init = init_state;
+    p.final_state = final_state;
+    p.states = (float*)(ws + pl.off_states);
+    p.decay = (float*)(ws + pl.off_decay);
+    p.L = d.seqlen;
+    p.ys_t = y_token_stride;
+    p.ys_h = y_head_stride;
+    p.nspan = pl.nspan;
+    p.batch = d.batch;
+    p.H = d.nheads;
+    p.P = d.headdim;
+    p.G = d.ngroups;
+    p.N = d.d_state;
+    p.nseq = d.nseq;
+    p.K = pl.K;
+    p.sps = pl.sps;
+    p.npg = pl.npg;
+    p.reverse = reverse;
+    p.d_init = d_init;
+
+    hipError_t e = hipSuccess;
+    if (d.nseq > 0) {
+        p.cu = (const int32_t*)(ws + pl.off_cu);
+        p.span_off = (const int32_t*)(ws + pl.off_spoff);
+        p.table = (const int4*)(ws + pl.off_table);
+        e = ssd::launch_span_table(cu_seqlens, d.nseq, T, pl.K, pl.nspan,
+                                   (int32_t*)(ws + pl.off_cu), (int32_t*)(ws + pl.off_spoff),
+                                   (int4*)(ws + pl.off_table), s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
+    e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    e = ssd::launch_state_pass(p, d.d_state, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    e = ssd::launch_span_scan(p, d.dtype, d.d_state, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // extern "C"

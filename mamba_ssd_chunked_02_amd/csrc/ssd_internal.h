@@ -1,0 +1,54 @@
+// Internal declarations shared by the C-ABI layer (ssd_api.hip) and the
+// kernels (ssd_kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kChunk = 64;     // tokens per chunk (one wavefront of lanes)
+constexpr int kWaves = 4;      // wavefronts per workgroup in the span kernels
+constexpr int kThreads = 256;  // kWaves * 64
+constexpr int kPGroup = 64;    // headdim columns per workgroup (16 per wave)
+constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Everything the kernels need, passed by value.
+struct KParams {
+    const void* x;          // [b, L, H, P]
+    const void* d_raw;      // [b, L, H]
+    const void* B;          // [b, L, G, N]
+    const void* C;          // [b, L, G, N]
+    void* y;                // strided output
+    const float* init;      // [S, H, N, P] or null
+    float* final_state;     // [S, H, N, P] or null
+    float* states;          // [nspan][H][P][N] span states / incoming states
+    float* decay;           // [nspan][H] span decay products
+    const int32_t* cu;      // sanitized cu_seqlens [nseq+1] (varlen) or null
+    const int32_t* span_off;// [nseq+1] first span of each sequence (varlen)
+    const int4* table;      // [nspan] {seq, chunk0, nchunks, 0} (varlen)
+    int64_t L;              // tokens per batch row
+    int64_t ys_t, ys_h;     // y strides (elements)
+    int64_t nspan;          // span slots (grid extent)
+    int32_t batch, H, P, G, N;
+    int32_t nseq;           // 0 = batch mode
+    int32_t K;              // chunks per span
+    int32_t sps;            // spans per sequence (batch mode)
+    int32_t npg;            // headdim column groups of kPGroup
+    int32_t reverse;
+    float d_init;
+};
+
+// Launchers (ssd_kernels.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,
+                             int32_t K, int64_t nspan, int32_t* cu_san,
+                             int32_t* span_off, int4* table, hipStream_t s);
+hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s);
+hipError_t launch_state_pass(const KParams& p, int N, hipStream_t s);
+hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
+
+// LDS bytes one span workgroup uses for (dtype, N, scan); 0 = not built.
+size_t span_lds_bytes(int dtype, int N, bool scan);
+
+}  // namespace ssd

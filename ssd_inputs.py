@@ -20,10 +20,16 @@ The five workloads are the shapes the pages use for the Mamba-2 SSD scan:
 * ``bidir``   -- 1 x 1,048,576 tokens, 8 heads x 192, d_state 64, run
   forward and reverse (view-synthesis row of the same table, §3.1/§3.2).
 
-Recipe: ``numpy.random.default_rng([seed, cfg_id])``; draw order X, B, C,
-d_raw, init_state, lengths; every draw is standard normal in float32, then
-rounded to bfloat16 (round to nearest even, via torch's cast) for the bf16
-workloads.  Values handed to the oracle are exactly the values the GPU reads.
+Recipe (``make_inputs``, on the host): ``numpy.random.default_rng([seed,
+cfg_id])``; draw order X, B, C, d_raw, init_state, lengths; every draw is
+standard normal in float32, then rounded to bfloat16 (round to nearest even,
+via torch's cast) for the bf16 workloads.  Values handed to the oracle are
+exactly the values the GPU reads.
+
+``make_inputs_device`` draws the same distributions with torch's Philox
+generator directly on a GPU (seed ``seed * 1000 + cfg_id``).  The 1M-token
+workload uses it because drawing 1.6e9 normals on the host takes minutes;
+parity checks then copy the sampled slices they need back to the host.
 """
 from __future__ import annotations
 
@@ -163,3 +169,32 @@ def random_problem(seed: int, batch: int, seqlen: int, nheads: int, headdim: int
         "cu_seqlens": cu,
         "d_init": float(np.float32(d_init)),
     }
+
+
+def make_inputs_device(w: Workload, device, seed: int = 0) -> dict:
+    """Like ``make_inputs`` but drawn on ``device`` with torch's generator
+    (different numbers from the host recipe; same shapes and distributions).
+    cu_seqlens still come from the host recipe's length generator."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 1000 + w.cfg_id)
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def draw(shape, scale=1.0):
+        t = torch.randn(shape, dtype=torch.float32, device=device, generator=gen)
+        if scale != 1.0:
+            t.mul_(scale)
+        return t
+
+    x = draw((b, L, H, P)).to(dt)
+    Bm = draw((b, L, G, N)).to(dt)
+    Cm = draw((b, L, G, N)).to(dt)
+    d_raw = draw((b, L, H)).to(dt)
+    init = draw((w.nstates, H, N, P), 0.1) if w.init == "normal0.1" else None
+    cu = None
+    if w.nseq:
+        rng = np.random.default_rng([seed, w.cfg_id])
+        lens = varlen_lengths(rng, w.nseq, w.tokens)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(device)
+    return {"x": x, "d_raw": d_raw, "B": Bm, "C": Cm, "init_state": init,
+            "cu_seqlens": cu, "d_init": float(np.float32(w.d_init))}

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every function include/ssd.h declares, and
+rejects bad arguments with the documented status before any HIP call.
+Calls that pass made-up device pointers only use argument sets that the
+host checks must reject; they are skipped where a GPU is visible so that a
+regression in the checks can never launch a kernel on such pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mamba_ssd_chunked_02_amd as m
+    m.library()
+    return m
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+def header_define(name):
+    return int(re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read()).group(1))
+
+
+def test_exports_every_declared_function(m):
+    lib = ctypes.CDLL(m._binding.LIB_PATH)
+    names = header_functions()
+    assert set(names) >= {"ssd_abi_version", "ssd_fwd", "ssd_fwd_workspace_bytes",
+                          "ssd_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(m):
+    assert m.ssd_abi_version() == header_define("SSD_ABI_VERSION")
+
+
+def test_status_strings(m):
+    codes = [int(v) for v in re.findall(r"SSD_(?:OK|ERR_\w+)\s*=\s*(-?\d+)", open(HEADER).read())]
+    assert 0 in codes and -7 in codes
+    for c in codes:
+        s = m.ssd_status_string(c)
+        assert s and "unknown ssd status" not in s
+    assert "unknown ssd status" in m.ssd_status_string(12345)
+
+
+def test_workspace_bytes(m):
+    from ssd_inputs import WORKLOADS
+    for w in WORKLOADS.values():
+        d = m.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups,
+                        w.chunk_size, w.nseq, m.SSD_BF16 if w.dtype == "bf16" else m.SSD_F32)
+        ws = m.ssd_fwd_workspace_bytes(d)
+        # the span states dominate: at most one N x P float state per chunk-head
+        nch = w.tokens // 64 + w.nseq + w.batch
+        assert 0 < ws <= nch * w.nheads * w.headdim * w.d_state * 4 + (1 << 20) * (1 + w.nseq)
+        assert ws % 256 == 0
+    assert m.ssd_fwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 16, chunk_size=32)) == 0
+    assert m.ssd_fwd_workspace_bytes(m.make_dims(1, 64, 2, 24, 16)) == 0
+    assert m.ssd_fwd_workspace_bytes(m.make_dims(2, 64, 2, 16, 16, nseq=3)) == 0
+
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below is rejected
+
+
+def call(m, dims, **kw):
+    args = dict(x=FAKE, d_raw=FAKE, d_init=-4.6, B=FAKE, C=FAKE, init=None, cu=None, reverse=0,
+                y=FAKE, yst=(dims.nheads * dims.headdim) if dims else 64,
+                ysh=dims.headdim if dims else 16, fin=None, ws=FAKE, wsb=1 << 40, stream=None)
+    args.update(kw)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)
+    return m.library().ssd_fwd(
+        ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)(), vp(args["x"]), vp(args["d_raw"]), args["d_init"], vp(args["B"]),
+        vp(args["C"]), vp(args["init"]), vp(args["cu"]), args["reverse"], vp(args["y"]),
+        args["yst"], args["ysh"], vp(args["fin"]), vp(args["ws"]), args["wsb"], vp(args["stream"]))
+
+
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="made-up pointers are only passed where no GPU exists")
+
+
+@needs_no_gpu
+def test_rejects_bad_arguments(m):
+    ok = m.make_dims(1, 128, 2, 64, 128)
+    assert call(m, None) == -1
+    assert call(m, ok, x=None) == -1                                   # NULL_ARG
+    assert call(m, ok, y=None) == -1
+    assert call(m, m.make_dims(1, 128, 2, 64, 128, dtype=7)) == -3     # DTYPE
+    assert call(m, m.make_dims(1, 128, 2, 64, 128, chunk_size=32)) == -5  # UNSUPPORTED
+    assert call(m, m.make_dims(1, 128, 2, 64, 48)) == -5
+    assert call(m, m.make_dims(1, 128, 2, 64, 256, dtype=0)) == -5
+    assert call(m, m.make_dims(1, 128, 2, 24, 128)) == -2              # SHAPE headdim
+    assert call(m, m.make_dims(1, 128, 3, 64, 128, ngroups=2)) == -2   # H % G
+    assert call(m, m.make_dims(2, 128, 2, 64, 128, nseq=2)) == -2      # varlen needs b == 1
+    assert call(m, m.make_dims(1, 128, 2, 64, 128, nseq=2)) == -1      # cu_seqlens missing
+    assert call(m, ok, cu=FAKE) == -2                                  # cu without nseq
+    assert call(m, ok, reverse=2) == -2
+    assert call(m, ok, x=FAKE + 8) == -4                               # ALIGN
+    assert call(m, ok, y=FAKE + 2) == -4
+    assert call(m, ok, yst=64 * 2 + 4) == -4
+    assert call(m, ok, ws=None) == -6                                  # WORKSPACE
+    assert call(m, ok, wsb=16) == -6
+    assert call(m, ok, ws=FAKE + 16) == -4
+
+
+def test_binding_rejects_cpu_mismatch(m):
+    x = torch.zeros(1, 64, 2, 16)
+    with pytest.raises(ValueError):
+        m.ssd_fwd(x, torch.zeros(1, 64, 3), -4.6, torch.zeros(1, 64, 1, 16),
+                  torch.zeros(1, 64, 1, 16))
