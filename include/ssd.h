@@ -111,6 +111,41 @@ int ssd_fwd(const ssd_dims* dims,
             void* workspace, size_t workspace_bytes,
             void* stream);
 
+/* How ssd_fwd splits a problem of these sizes (a pure function of *dims). */
+typedef struct ssd_plan_info {
+    int32_t chunks_per_span;   /* 64-token chunks walked by one workgroup; the
+                                  state stays on chip inside a span          */
+    int32_t col_groups;        /* headdim columns are split in groups of 64  */
+    int64_t nspan;             /* span slots (upper bound with cu_seqlens)   */
+    uint64_t workspace_bytes;  /* = ssd_fwd_workspace_bytes(dims)            */
+} ssd_plan_info;
+
+/* Fills *out for these sizes; returns the status ssd_fwd's size checks
+ * would give. */
+int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out);
+
+/* Stages of ssd_fwd, one kernel launch each, in this order. */
+enum {
+    SSD_STAGE_TABLE = 1,  /* span table from cu_seqlens (no-op without them) */
+    SSD_STAGE_STATE = 2,  /* per-span local states and decays               */
+    SSD_STAGE_PASS = 4,   /* state passing across spans, final_state        */
+    SSD_STAGE_SCAN = 8,   /* per-chunk outputs y                            */
+    SSD_STAGE_ALL = 15
+};
+
+/* ssd_fwd restricted to the stages in stage_mask, for callers that time or
+ * interleave work between stages.  Same arguments and checks as ssd_fwd;
+ * running the stages in the order above on one stream with one workspace
+ * (left untouched in between) gives exactly ssd_fwd's result. */
+int ssd_fwd_stages(uint32_t stage_mask, const ssd_dims* dims,
+                   const void* x, const void* d_raw, float d_init,
+                   const void* B, const void* C,
+                   const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+                   void* y, int64_t y_token_stride, int64_t y_head_stride,
+                   float* final_state,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);
 

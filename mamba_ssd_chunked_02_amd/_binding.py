@@ -37,6 +37,19 @@ class SsdDims(ctypes.Structure):
     ]
 
 
+STAGE_TABLE, STAGE_STATE, STAGE_PASS, STAGE_SCAN, STAGE_ALL = 1, 2, 4, 8, 15
+
+
+class SsdPlanInfo(ctypes.Structure):
+    """Mirror of ``ssd_plan_info`` in include/ssd.h."""
+    _fields_ = [
+        ("chunks_per_span", ctypes.c_int32),
+        ("col_groups", ctypes.c_int32),
+        ("nspan", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+
 class SsdError(RuntimeError):
     def __init__(self, status: int, where: str = "ssd_fwd"):
         self.status = status
@@ -60,8 +73,7 @@ def library() -> ctypes.CDLL:
         lib.ssd_fwd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims)]
         lib.ssd_status_string.restype = ctypes.c_char_p
         lib.ssd_status_string.argtypes = [ctypes.c_int]
-        lib.ssd_fwd.restype = ctypes.c_int
-        lib.ssd_fwd.argtypes = [
+        fwd_args = [
             ctypes.POINTER(SsdDims),
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_void_p,
@@ -71,6 +83,12 @@ def library() -> ctypes.CDLL:
             ctypes.c_void_p, ctypes.c_size_t,
             ctypes.c_void_p,
         ]
+        lib.ssd_fwd.restype = ctypes.c_int
+        lib.ssd_fwd.argtypes = fwd_args
+        lib.ssd_fwd_stages.restype = ctypes.c_int
+        lib.ssd_fwd_stages.argtypes = [ctypes.c_uint32] + fwd_args
+        lib.ssd_fwd_plan.restype = ctypes.c_int
+        lib.ssd_fwd_plan.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(SsdPlanInfo)]
         _lib = lib
     return _lib
 
@@ -93,6 +111,14 @@ def ssd_fwd_workspace_bytes(dims: SsdDims) -> int:
     return int(library().ssd_fwd_workspace_bytes(ctypes.byref(dims)))
 
 
+def ssd_fwd_plan(dims: SsdDims) -> SsdPlanInfo:
+    info = SsdPlanInfo()
+    rc = library().ssd_fwd_plan(ctypes.byref(dims), ctypes.byref(info))
+    if rc != 0:
+        raise SsdError(rc, "ssd_fwd_plan")
+    return info
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -106,6 +132,34 @@ def dims_for(x, B, chunk_size=CHUNK, cu_seqlens=None) -> SsdDims:
     return make_dims(b, L, H, P, N, G, chunk_size, nseq, _DTYPES[x.dtype])
 
 
+class PreparedCall:
+    """Marshalled arguments of one ssd_fwd call (tensors kept alive), so a
+    loop can launch the same problem repeatedly with no re-marshalling."""
+
+    def __init__(self, dims, args, keep, y, final_state, workspace):
+        self.dims = dims
+        self.args = args
+        self._keep = keep
+        self.y = y
+        self.final_state = final_state
+        self.workspace = workspace
+
+    def run(self, stages: int = STAGE_ALL, stream=None):
+        """Launch the given stages on ``stream`` (torch's current stream of
+        the tensors' device by default)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.y.device).cuda_stream
+        lib = library()
+        if stages == STAGE_ALL:
+            rc = lib.ssd_fwd(ctypes.byref(self.dims), *self.args, ctypes.c_void_p(stream))
+        else:
+            rc = lib.ssd_fwd_stages(stages, ctypes.byref(self.dims), *self.args,
+                                    ctypes.c_void_p(stream))
+        if rc != 0:
+            raise SsdError(rc)
+        return self.y, self.final_state
+
+
 def ssd_fwd(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlens=None,
             reverse=False, y=None, final_state=True, workspace=None):
     """Run the SSD forward scan on the GPU.
@@ -117,6 +171,16 @@ def ssd_fwd(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlen
     ``final_state=False`` to skip it or a [S,H,N,P] fp32 tensor to fill.
     Returns (y, final_state or None).  Launches on torch's current stream.
     """
+    call = prepare(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, reverse, y,
+                   final_state, workspace)
+    with torch.cuda.device(x.device):
+        return call.run()
+
+
+def prepare(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlens=None,
+            reverse=False, y=None, final_state=True, workspace=None) -> PreparedCall:
+    """Check and marshal the arguments of ``ssd_fwd``; allocate y,
+    final_state and the workspace when not given."""
     if x.dim() != 4 or d_raw.dim() != 3 or B.dim() != 4 or C.dim() != 4:
         raise ValueError("x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] expected")
     b, L, H, P = x.shape
@@ -158,16 +222,12 @@ def ssd_fwd(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlen
     need = ssd_fwd_workspace_bytes(dims)  # 0 for invalid sizes: ssd_fwd reports why
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    with torch.cuda.device(dev):
-        rc = library().ssd_fwd(
-            ctypes.byref(dims), _ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
+    args = (_ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
             _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0,
             _ptr(y), y.stride(1), y.stride(2), _ptr(final_state),
-            _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
-    if rc != 0:
-        raise SsdError(rc)
-    return y, final_state
+            _ptr(workspace), workspace.numel())
+    keep = (x, d_raw, B, C, init_state, cu_seqlens)
+    return PreparedCall(dims, args, keep, y, final_state, workspace)
 
 
 def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,

@@ -23,6 +23,8 @@ struct Plan {
     int32_t K = 1;          // chunks per span
     int32_t sps = 0;        // spans per sequence (batch mode)
     int32_t npg = 0;        // headdim column groups
+    int32_t hg_state = 1;   // heads per span_state workgroup
+    int32_t hg_scan = 1;    // heads per span_scan workgroup
     int64_t nspan = 0;      // span slots
     size_t off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
     size_t total = 0;
@@ -30,16 +32,29 @@ struct Plan {
 
 // Chunks per span: the state stays on chip inside a span and only span
 // borders go through HBM, so longer spans move fewer bytes; but each span is
-// walked by one workgroup, so spans are kept short enough that the grid
-// still holds >= 2048 workgroups (8 per CU).  SSD_SPAN_CHUNKS overrides it.
-int32_t choose_k(int64_t chunk_units) {
+// walked by one workgroup, so spans stay short enough that the span_scan grid
+// keeps >= 4096 workgroups (16 per CU) once past two chunks.
+// SSD_SPAN_CHUNKS overrides it (tuning sweeps).
+int32_t choose_k(int64_t nch, int64_t groups) {
     if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
         const int v = atoi(e);
         if (v >= 1 && v <= 64) return v;
     }
-    int32_t K = 1;
-    while (K < 8 && chunk_units / (2 * K) >= 2048) K *= 2;
+    int32_t K = 2;
+    while (K < 8 && ceil_div(nch, K) * groups >= 4096) K *= 2;
     return K;
+}
+
+// Heads per workgroup: `dflt` unless the named environment variable asks
+// for another of 1, 2 or 4 up to `most` (tuning sweeps).  span_state runs one
+// head per workgroup by default (more, smaller workgroups overlap their load
+// and store phases better); span_scan shares the C B^T tiles across heads.
+int32_t heads_override(const char* name, int32_t dflt, int32_t most) {
+    if (const char* e = getenv(name)) {
+        const int v = atoi(e);
+        if ((v == 1 || v == 2 || v == 4) && v <= most) return v;
+    }
+    return dflt < most ? dflt : most;
 }
 
 int make_plan(const ssd_dims* d, Plan* pl) {
@@ -58,9 +73,16 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     if (T > ((int64_t)1 << 40)) return SSD_ERR_SHAPE;
 
     pl->npg = (int32_t)ceil_div(d->headdim, kPGroup);
+    // heads per workgroup: as many as the kernel carries, all in one B/C group
+    const int32_t hpg = d->nheads / d->ngroups;
+    pl->hg_state = heads_override("SSD_HEADS_STATE", 1, ssd::span_max_heads(d->d_state, false));
+    while (hpg % pl->hg_state) pl->hg_state /= 2;
+    pl->hg_scan = heads_override("SSD_HEADS_SCAN", ssd::span_max_heads(d->d_state, true),
+                                 ssd::span_max_heads(d->d_state, true));
+    while (hpg % pl->hg_scan) pl->hg_scan /= 2;
     const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
                                           : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);
-    pl->K = choose_k(nch_bound * d->nheads * pl->npg);
+    pl->K = choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg);
     if (d->nseq > 0) {
         pl->sps = 0;
         pl->nspan = ceil_div(T, (int64_t)kChunk * pl->K) + d->nseq;
@@ -70,7 +92,8 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     }
     size_t off = 0;
     pl->off_states = off;
-    off = align_up(off + (size_t)pl->nspan * d->nheads * d->headdim * d->d_state * sizeof(float));
+    const size_t esz = d->dtype == SSD_BF16 ? 2 : 4;  // span states use the input type
+    off = align_up(off + (size_t)pl->nspan * d->nheads * d->headdim * d->d_state * esz);
     pl->off_decay = off;
     off = align_up(off + (size_t)pl->nspan * d->nheads * sizeof(float));
     if (d->nseq > 0) {
@@ -130,10 +153,33 @@ const char* ssd_status_string(int status) {
     return "unknown ssd status";
 }
 
+int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out) {
+    Plan pl;
+    const int st = make_plan(dims, &pl);
+    if (st != SSD_OK) return st;
+    if (!out) return SSD_ERR_NULL_ARG;
+    out->chunks_per_span = pl.K;
+    out->col_groups = pl.npg;
+    out->nspan = pl.nspan;
+    out->workspace_bytes = pl.total;
+    return SSD_OK;
+}
+
 int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init, const void* B,
             const void* C, const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
             void* y, int64_t y_token_stride, int64_t y_head_stride, float* final_state,
             void* workspace, size_t workspace_bytes, void* stream) {
+    return ssd_fwd_stages(SSD_STAGE_ALL, dims, x, d_raw, d_init, B, C, init_state, cu_seqlens,
+                          reverse, y, y_token_stride, y_head_stride, final_state, workspace,
+                          workspace_bytes, stream);
+}
+
+int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const void* d_raw,
+                   float d_init, const void* B, const void* C, const float* init_state,
+                   const int32_t* cu_seqlens, int32_t reverse, void* y, int64_t y_token_stride,
+                   int64_t y_head_stride, float* final_state, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (mask & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_SHAPE;
     Plan pl;
     const int st = make_plan(dims, &pl);
     if (st != SSD_OK) return st;
@@ -154,7 +200,7 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
         if ((uintptr_t)workspace % kAlign) return SSD_ERR_ALIGN;
     }
     hipStream_t s = (hipStream_t)stream;
-    if (d.nseq > 0) {
+    if (d.nseq > 0 && (mask & SSD_STAGE_TABLE)) {
         const char* chk = getenv("SSD_CHECK");
         if (chk && chk[0] == '1') {
             const int c = check_cu(cu_seqlens, d.nseq, T, s);
@@ -172,7 +218,7 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     p.y = y;
     p.init = init_state;
     p.final_state = final_state;
-    p.states = (float*)(ws + pl.off_states);
+    p.states = ws + pl.off_states;
     p.decay = (float*)(ws + pl.off_decay);
     p.L = d.seqlen;
     p.ys_t = y_token_stride;
@@ -187,6 +233,8 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     p.K = pl.K;
     p.sps = pl.sps;
     p.npg = pl.npg;
+    p.hg_state = pl.hg_state;
+    p.hg_scan = pl.hg_scan;
     p.reverse = reverse;
     p.d_init = d_init;
 
@@ -195,17 +243,25 @@ int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
         p.cu = (const int32_t*)(ws + pl.off_cu);
         p.span_off = (const int32_t*)(ws + pl.off_spoff);
         p.table = (const int4*)(ws + pl.off_table);
-        e = ssd::launch_span_table(cu_seqlens, d.nseq, T, pl.K, pl.nspan,
-                                   (int32_t*)(ws + pl.off_cu), (int32_t*)(ws + pl.off_spoff),
-                                   (int4*)(ws + pl.off_table), s);
+        if (mask & SSD_STAGE_TABLE) {
+            e = ssd::launch_span_table(cu_seqlens, d.nseq, T, pl.K, pl.nspan,
+                                       (int32_t*)(ws + pl.off_cu), (int32_t*)(ws + pl.off_spoff),
+                                       (int4*)(ws + pl.off_table), s);
+            if (e != hipSuccess) return SSD_ERR_HIP;
+        }
+    }
+    if (mask & SSD_STAGE_STATE) {
+        e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
-    e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_state_pass(p, d.d_state, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
-    e = ssd::launch_span_scan(p, d.dtype, d.d_state, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
+    if (mask & SSD_STAGE_PASS) {
+        e = ssd::launch_state_pass(p, d.dtype, s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
+    if (mask & SSD_STAGE_SCAN) {
+        e = ssd::launch_span_scan(p, d.dtype, d.d_state, s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
     return SSD_OK;
 }
 

@@ -23,7 +23,8 @@ struct KParams {
     void* y;                // strided output
     const float* init;      // [S, H, N, P] or null
     float* final_state;     // [S, H, N, P] or null
-    float* states;          // [nspan][H][P][N] span states / incoming states
+    void* states;           // [nspan][H][P][N] span states / incoming states,
+                            // stored in the input type (accumulated in fp32)
     float* decay;           // [nspan][H] span decay products
     const int32_t* cu;      // sanitized cu_seqlens [nseq+1] (varlen) or null
     const int32_t* span_off;// [nseq+1] first span of each sequence (varlen)
@@ -36,6 +37,8 @@ struct KParams {
     int32_t K;              // chunks per span
     int32_t sps;            // spans per sequence (batch mode)
     int32_t npg;            // headdim column groups of kPGroup
+    int32_t hg_state;       // heads per span_state workgroup (divides H/G)
+    int32_t hg_scan;        // heads per span_scan workgroup (divides H/G)
     int32_t reverse;
     float d_init;
 };
@@ -45,8 +48,11 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,
                              int32_t K, int64_t nspan, int32_t* cu_san,
                              int32_t* span_off, int4* table, hipStream_t s);
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s);
-hipError_t launch_state_pass(const KParams& p, int N, hipStream_t s);
+hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s);
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
+
+// Most heads one span workgroup can carry for this d_state.
+int span_max_heads(int N, bool scan);
 
 // LDS bytes one span workgroup uses for (dtype, N, scan); 0 = not built.
 size_t span_lds_bytes(int dtype, int N, bool scan);
