@@ -33,26 +33,26 @@ struct Plan {
 // Chunks per span: the state stays on chip inside a span and only span
 // borders go through HBM, so longer spans move fewer bytes; but each span is
 // walked by one workgroup, so spans stay short enough that the span_scan grid
-// keeps >= 4096 workgroups (16 per CU) once past two chunks.
+// keeps >= 4096 workgroups (16 per CU) once past four chunks.
 // SSD_SPAN_CHUNKS overrides it (tuning sweeps).
 int32_t choose_k(int64_t nch, int64_t groups) {
     if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
         const int v = atoi(e);
         if (v >= 1 && v <= 64) return v;
     }
-    int32_t K = 2;
+    int32_t K = 4;
     while (K < 8 && ceil_div(nch, K) * groups >= 4096) K *= 2;
     return K;
 }
 
 // Heads per workgroup: `dflt` unless the named environment variable asks
-// for another of 1, 2 or 4 up to `most` (tuning sweeps).  span_state runs one
-// head per workgroup by default (more, smaller workgroups overlap their load
-// and store phases better); span_scan shares the C B^T tiles across heads.
+// for 1 or 2 up to `most` (tuning sweeps).  Both span kernels run one head
+// per workgroup by default: more, smaller workgroups overlap their load,
+// compute and store phases better than wider ones sharing B and C.
 int32_t heads_override(const char* name, int32_t dflt, int32_t most) {
     if (const char* e = getenv(name)) {
         const int v = atoi(e);
-        if ((v == 1 || v == 2 || v == 4) && v <= most) return v;
+        if ((v == 1 || v == 2) && v <= most) return v;
     }
     return dflt < most ? dflt : most;
 }
@@ -75,10 +75,9 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     pl->npg = (int32_t)ceil_div(d->headdim, kPGroup);
     // heads per workgroup: as many as the kernel carries, all in one B/C group
     const int32_t hpg = d->nheads / d->ngroups;
-    pl->hg_state = heads_override("SSD_HEADS_STATE", 1, ssd::span_max_heads(d->d_state, false));
+    pl->hg_state = heads_override("SSD_HEADS_STATE", 1, ssd::span_max_heads(d->dtype, d->d_state, false));
     while (hpg % pl->hg_state) pl->hg_state /= 2;
-    pl->hg_scan = heads_override("SSD_HEADS_SCAN", ssd::span_max_heads(d->d_state, true),
-                                 ssd::span_max_heads(d->d_state, true));
+    pl->hg_scan = heads_override("SSD_HEADS_SCAN", 1, ssd::span_max_heads(d->dtype, d->d_state, true));
     while (hpg % pl->hg_scan) pl->hg_scan /= 2;
     const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
                                           : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);

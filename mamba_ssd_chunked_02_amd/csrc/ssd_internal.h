@@ -52,7 +52,7 @@ hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s);
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
 
 // Most heads one span workgroup can carry for this d_state.
-int span_max_heads(int N, bool scan);
+int span_max_heads(int dtype, int N, bool scan);
 
 // LDS bytes one span workgroup uses for (dtype, N, scan); 0 = not built.
 size_t span_lds_bytes(int dtype, int N, bool scan);

@@ -112,33 +112,95 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
 }
 __device__ __forceinline__ f32x4 load4(const float* p) { return *(const f32x4*)p; }
 
-// Compile-time shape of one span workgroup: HG heads (sharing one B/C group)
-// x 64 headdim columns, one 16-column block per wave.
+// Compile-time shape of one span workgroup: HG heads sharing one B/C group,
+// one quad of 4 waves per head, each wave one 16-column block of the 64
+// headdim columns of the group.
 template <typename T, int N, int HG>
 struct Cfg {
+    static constexpr int TH = kThreads * HG;     // threads per workgroup
+    static constexpr int NW = TH / 64;           // waves per workgroup
     static constexpr int NB = N / 16;            // 16-row blocks of the state
     static constexpr int KN = (N + 31) / 32;     // K=32 steps over the state dim
     static constexpr int EPU = 16 / sizeof(T);   // elements per 16-byte unit
-    static constexpr int XP = kPGroup + EPU;     // row pitch of X tiles (elements)
-    static constexpr int NP = N + EPU;           // row pitch of B / C tiles
     static constexpr int XU = kPGroup / EPU;     // 16-byte units per X row
     static constexpr int BU = N / EPU;           // 16-byte units per B / C row
-    static constexpr int XIT = kChunk * XU / kThreads;
-    static constexpr int BIT = (kChunk * BU + kThreads - 1) / kThreads;
 };
 
-// Heads per workgroup: the span_state kernel keeps HG states of N x 16 per
-// wave in registers, span_scan also the output tiles, so it carries fewer.
-constexpr int heads_state(int N) { return N <= 128 ? 4 : 2; }
-constexpr int heads_scan(int N) { return N <= 128 ? 2 : 1; }
+// Heads (quads) per workgroup: up to 2 (8 waves), one for the scan when a
+// state row is wider than 256 bytes (its per-wave registers exceed 256).
+constexpr int heads_state(int N, int esz) { return 2; }
+constexpr int heads_scan(int N, int esz) { return N * esz <= 256 ? 2 : 1; }
 
 // Wave index within the workgroup as a scalar, so branches on it stay uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false);
+    return v + __int_as_float(t);
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Raw v_exp_f32: every argument here is <= 0, results below 2^-126 flush to 0.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Token-contracted MFMA fragment from a natural [token][col] LDS tile: this
+// LDS tiles are 64 token rows of U 16-byte units, unpadded; unit u of row r
+// sits at unit u ^ (r & M) (M = min(U, 8) - 1), which spreads the 16-row
+// column reads of the MFMA operands over all banks.  swz() gives the element
+// offset of (row r, column e).
+template <int U, int EPU>
+__device__ __forceinline__ int swz(int r, int e) {
+    constexpr int M = (U < 8 ? U : 8) - 1;
+    return r * (U * EPU) + (((e / EPU) ^ (r & M)) * EPU) + (e % EPU);
+}
+
+// Issue the direct global -> LDS loads (global_load_lds_dwordx4) of one tile:
+// instruction i fills physical units 64i .. 64i+63, lane l the unit 64i + l.
+// Rows past the chunk read row 0 and columns past `ucols` read unit 0: such
+// entries only ever meet zero weights.  `rowp(r)` is the global row pointer.
+template <int U, int EPU, typename T, typename RowPtr>
+__device__ __forceinline__ void issue_tile(T* tile, int first, int step, int clen, int ucols,
+                                           int lane, RowPtr rowp) {
+    constexpr int M = (U < 8 ? U : 8) - 1;
+#pragma unroll
+    for (int i = first; i < U; i += step) {
+        const int pu = 64 * i + lane;
+        const int r = pu / U;
+        int u = (pu % U) ^ (r & M);
+        if (u >= ucols) u = 0;
+        const T* g = rowp(r < clen ? r : 0) + u * EPU;
+        __builtin_amdgcn_global_load_lds((const void*)g,
+                                         (__attribute__((address_space(3))) void*)(tile + 64 * i * EPU),
+                                         16, 0, 0);
+    }
+}
+
+// 8 / 4 consecutive elements of a swizzled tile (e a multiple of 8 / 4).
+template <int U>
+__device__ __forceinline__ bf16x8 lds8(const bf16* t, int r, int e) { return ld8(t + swz<U, 8>(r, e)); }
+template <int U>
+__device__ __forceinline__ f32x8 lds8(const float* t, int r, int e) {
+    return cat<f32x8, f32x4>(ld4(t + swz<U, 4>(r, e)), ld4(t + swz<U, 4>(r, e + 4)));
+}
+template <int U>
+__device__ __forceinline__ bf16x4 lds4(const bf16* t, int r, int e) { return ld4(t + swz<U, 8>(r, e)); }
+template <int U>
+__device__ __forceinline__ f32x4 lds4(const float* t, int r, int e) { return ld4(t + swz<U, 4>(r, e)); }
+
+// Token-contracted MFMA fragment from a swizzled [token][col] tile: this
 // lane's column c0 + lane%16 at tokens r0..r0+3 (slots 0-3) and r1..r1+3
 // (slots 4-7); r0, r1 are the same for the 16 lanes of a group.  bf16 uses
 // the gfx950 transposing read (ds_read_b64_tr_b16): lane i of a 16-lane
@@ -151,22 +213,21 @@ __device__ __forceinline__ bf16x4 ldtr(const bf16* p) {
         (__attribute__((address_space(3))) s16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
-__device__ __forceinline__ bf16x8 tok_frag(const bf16* tile, int pitch, int r0, int r1, int c0,
-                                           int lane) {
-    const int j = lane & 15;
-    const bf16* q = tile + (j >> 2) * pitch + c0 + 4 * (j & 3);
-    return cat<bf16x8, bf16x4>(ldtr(q + r0 * pitch), ldtr(q + r1 * pitch));
+template <int U>
+__device__ __forceinline__ bf16x8 tok_frag(const bf16* t, int r0, int r1, int c0, int lane) {
+    const int j = lane & 15, dr = j >> 2, e = c0 + 4 * (j & 3);
+    return cat<bf16x8, bf16x4>(ldtr(t + swz<U, 8>(r0 + dr, e)), ldtr(t + swz<U, 8>(r1 + dr, e)));
 }
-__device__ __forceinline__ f32x8 tok_frag(const float* tile, int pitch, int r0, int r1, int c0,
-                                          int lane) {
-    const float* q = tile + c0 + (lane & 15);
-    f32x8 r;
+template <int U>
+__device__ __forceinline__ f32x8 tok_frag(const float* t, int r0, int r1, int c0, int lane) {
+    const int e = c0 + (lane & 15);
+    f32x8 v;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        r[k] = q[(r0 + k) * pitch];
-        r[4 + k] = q[(r1 + k) * pitch];
+        v[k] = t[swz<U, 4>(r0 + k, e)];
+        v[4 + k] = t[swz<U, 4>(r1 + k, e)];
     }
-    return r;
+    return v;
 }
 
 // Per-head, per-chunk decay factors (cs = within-chunk cumulative -d in log2
@@ -199,28 +260,16 @@ __device__ __forceinline__ int64_t state_off(int pb, int nb, int lane, int NB) {
     return ((int64_t)(pb * NB + nb) * 64 + lane) * 4;
 }
 
-// LDS of one span workgroup: natural [token][column] tiles, rows padded by
-// 16 bytes.
+// LDS of one span workgroup.
 template <typename T, int N, int HG, bool SCAN>
 struct __attribute__((aligned(16))) Smem {
     using C = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
-    T xs[HG][kChunk][C::XP];          // X of every head, this group's 64 columns
-    T bs[kChunk][C::NP];              // B
-    T cs[SCAN ? kChunk : 1][C::NP];   // C                               (scan only)
-    X8 lf[SCAN ? HG : 1][6][64];      // masked C B^T fragments per head (scan only)
+    T xs[HG][kChunk * kPGroup];        // X of every head, this group's 64 columns
+    T bs[kChunk * N];                  // B
+    T cs[SCAN ? kChunk * N : 1];       // C                               (scan only)
+    X8 lf[SCAN ? HG : 1][6][64];       // masked C B^T fragments per head (scan only)
     Decay dec[HG];
-};
-
-// Global -> register staging of one chunk, prefetched one chunk ahead; 16-byte
-// units, consecutive lanes along a row.
-template <typename T, int N, int HG, bool SCAN>
-struct Stage {
-    using C = Cfg<T, N, HG>;
-    uint4 xr[HG][C::XIT];
-    uint4 br[C::BIT];
-    uint4 cr[SCAN ? C::BIT : 1];
-    float draw;  // d_raw of token lane for head `wave`
 };
 
 struct ChunkPos {
@@ -233,122 +282,76 @@ struct ChunkPos {
     }
 };
 
-// Issue every global load of one chunk into registers.
+// Issue every global load of one chunk: quad q's X tile (head h0 + q) and
+// all of B / C straight into LDS; the first wave of each quad also loads its
+// head's d_raw, one token per lane, into a register.
 template <typename T, int N, int HG, bool SCAN>
-__device__ __forceinline__ void load_chunk(Stage<T, N, HG, SCAN>& st, const KParams& p,
-                                           const ChunkPos& cp, int h0, int nh, int grp,
-                                           int pcol0, int xun) {
+__device__ __forceinline__ float issue_chunk(Smem<T, N, HG, SCAN>& sm, const KParams& p,
+                                             const ChunkPos& cp, int h0, int nh, int grp,
+                                             int pcol0, int xun) {
     using C = Cfg<T, N, HG>;
-    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-    const int64_t HP = (int64_t)p.H * p.P;
-    const T* xg = (const T*)p.x + (int64_t)h0 * p.P + pcol0;
-#pragma unroll
-    for (int it = 0; it < C::XIT; ++it) {
-        const int u = tid + it * kThreads;
-        const int s = u / C::XU, c = u % C::XU;
-        const bool ok = c < xun && s < cp.clen;
-        const T* row = xg + (ok ? cp.tok(s) : 0) * HP + c * C::EPU;
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ok && hh < nh) v = *(const uint4*)(row + hh * p.P);
-            st.xr[hh][it] = v;
-        }
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const int q = wave >> 2, w4 = wave & 3;
+    const int64_t HP = (int64_t)p.H * p.P, GN = (int64_t)p.G * N;
+    if (q < nh) {
+        const T* xh = (const T*)p.x + (int64_t)(h0 + q) * p.P + pcol0;
+        issue_tile<C::XU, C::EPU>(sm.xs[q], w4, 4, cp.clen, xun, lane,
+                                  [&](int r) { return xh + cp.tok(r) * HP; });
     }
     const T* bg = (const T*)p.B + (int64_t)grp * N;
-    const T* cg = (const T*)p.C + (int64_t)grp * N;
-    const int64_t GN = (int64_t)p.G * N;
-#pragma unroll
-    for (int it = 0; it < C::BIT; ++it) {
-        const int u = tid + it * kThreads;
-        const int s = u / C::BU, c = u % C::BU;
-        uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
-        if (u < kChunk * C::BU && s < cp.clen) {
-            const int64_t off = cp.tok(s) * GN + c * C::EPU;
-            vb = *(const uint4*)(bg + off);
-            if (SCAN) vc = *(const uint4*)(cg + off);
-        }
-        st.br[it] = vb;
-        if (SCAN) st.cr[it] = vc;
+    issue_tile<C::BU, C::EPU>(sm.bs, wave, C::NW, cp.clen, C::BU, lane,
+                              [&](int r) { return bg + cp.tok(r) * GN; });
+    if (SCAN) {
+        const T* cg = (const T*)p.C + (int64_t)grp * N;
+        issue_tile<C::BU, C::EPU>(sm.cs, wave, C::NW, cp.clen, C::BU, lane,
+                                  [&](int r) { return cg + cp.tok(r) * GN; });
     }
-    {
-        const int hh = wave;  // wave hh holds head hh's d_raw, one token per lane
-        float v = 0.f;
-        if (hh < nh && lane < cp.clen) v = (float)((const T*)p.d_raw)[cp.tok(lane) * p.H + h0 + hh];
-        st.draw = v;
-    }
+    float v = 0.f;
+    if (w4 == 0 && q < nh && lane < cp.clen)
+        v = (float)((const T*)p.d_raw)[cp.tok(lane) * p.H + h0 + q];
+    return v;
 }
 
-// Registers -> LDS for one chunk; wave hh also forms head hh's decay factors.
-template <typename T, int N, int HG, bool SCAN>
-__device__ __forceinline__ void write_chunk(Smem<T, N, HG, SCAN>& sm,
-                                            const Stage<T, N, HG, SCAN>& st,
-                                            const ChunkPos& cp, float d_init, int nh) {
-    using C = Cfg<T, N, HG>;
-    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-#pragma unroll
-    for (int it = 0; it < C::XIT; ++it) {
-        const int u = tid + it * kThreads;
-        const int s = u / C::XU, c = u % C::XU;
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh)
-            if (hh < nh) *(uint4*)&sm.xs[hh][s][c * C::EPU] = st.xr[hh][it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::BIT; ++it) {
-        const int u = tid + it * kThreads;
-        const int s = u / C::BU, c = u % C::BU;
-        if (u < kChunk * C::BU) {
-            *(uint4*)&sm.bs[s][c * C::EPU] = st.br[it];
-            if (SCAN) *(uint4*)&sm.cs[s][c * C::EPU] = st.cr[it];
-        }
-    }
-    if (wave < nh && wave < HG) {
-        // step sizes, their within-chunk prefix sum and the decay factors of
-        // head `wave`, one lane per token
-        Decay& D = sm.dec[wave];
-        const float dt = lane < cp.clen ? softplus(st.draw + d_init) : 0.f;
-        float v = -dt * kLog2e;
-#pragma unroll
-        for (int off = 1; off < kChunk; off <<= 1) {
-            const float o = __shfl_up(v, off, kChunk);
-            if (lane >= off) v += o;
-        }
-        const float c1 = __shfl(v, 15, kChunk), c2 = __shfl(v, 31, kChunk);
-        const float c3 = __shfl(v, 47, kChunk), c4 = __shfl(v, 63, kChunk);
-        const int sb = lane >> 4;
-        const float cbeg = sb == 0 ? 0.f : (sb == 1 ? c1 : (sb == 2 ? c2 : c3));
-        const float cend = sb == 0 ? c1 : (sb == 1 ? c2 : (sb == 2 ? c3 : c4));
-        D.cs2[lane] = v;
-        D.dt[lane] = dt;
-        D.w[lane] = fexp2(c4 - v) * dt;
-        D.fa[lane] = fexp2(cend - v) * dt;
-        D.fb[lane] = fexp2(v - cbeg);
-        D.fe[lane] = fexp2(v);
-        if (lane < 6) {
-            // (tb, sb) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): 2^{c_tb - c_{sb+1}}
-            const float ct = lane == 0 ? c1 : (lane < 3 ? c2 : c3);
-            const float cs = (lane == 0 || lane == 1 || lane == 3) ? c1 : ((lane == 2 || lane == 4) ? c2 : c3);
-            D.fm[lane] = fexp2(ct - cs);
-        }
+// The first wave of quad q forms head h0 + q's decay factors.
+__device__ __forceinline__ void decay_factors(Decay& D, float draw, float d_init, int clen,
+                                              int lane) {
+    const float dt = lane < clen ? softplus(draw + d_init) : 0.f;
+    const float v = wave_prefix_sum(-dt * kLog2e);
+    const float c1 = lane_value(v, 15), c2 = lane_value(v, 31);
+    const float c3 = lane_value(v, 47), c4 = lane_value(v, 63);
+    const int sb = lane >> 4;
+    const float cbeg = sb == 0 ? 0.f : (sb == 1 ? c1 : (sb == 2 ? c2 : c3));
+    const float cend = sb == 0 ? c1 : (sb == 1 ? c2 : (sb == 2 ? c3 : c4));
+    D.cs2[lane] = v;
+    D.dt[lane] = dt;
+    D.w[lane] = fexp2(c4 - v) * dt;
+    D.fa[lane] = fexp2(cend - v) * dt;
+    D.fb[lane] = fexp2(v - cbeg);
+    D.fe[lane] = fexp2(v);
+    if (lane < 6) {
+        // (tb, sb) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): 2^{c_tb - c_{sb+1}}
+        const float ct = lane == 0 ? c1 : (lane < 3 ? c2 : c3);
+        const float cs = (lane == 0 || lane == 1 || lane == 3) ? c1 : ((lane == 2 || lane == 4) ? c2 : c3);
+        D.fm[lane] = fexp2(ct - cs);
     }
 }
 
 // C B^T tiles of s-block SB (t-blocks tb >= SB: row s = 16*SB + 4g + i,
-// column t = 16*tb + l16 of the MFMA result), then for every head the tiles
-// times the decay mask, rounded, as halves of the intra-chunk B fragments.
+// column t = 16*tb + l16 of the MFMA result), times head q's decay mask,
+// rounded, as halves of q's intra-chunk B fragments.
 template <int SB, typename T, int N, int HG, bool SCAN>
-__device__ __forceinline__ void mask_phase(Smem<T, N, HG, SCAN>& sm, int nh, int lane) {
+__device__ __forceinline__ void mask_phase(Smem<T, N, HG, SCAN>& sm, int q, int lane) {
+    using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
-    constexpr int KN = Cfg<T, N, HG>::KN;
+    constexpr int KN = Cf::KN, BU = Cf::BU;
     const int l16 = lane & 15, g = lane >> 4;
     X8 a[KN];  // B rows 16*SB + l16, n = 32kk + 8g ..
 #pragma unroll
     for (int kk = 0; kk < KN; ++kk) {
         const int n = 32 * kk + 8 * g;
         a[kk] = X8{};
-        if (N % 32 == 0 || n < N) a[kk] = ld8(&sm.bs[16 * SB + l16][n]);
+        if (N % 32 == 0 || n < N) a[kk] = lds8<BU>(sm.bs, 16 * SB + l16, n);
     }
     f32x4 cbt[4];
 #pragma unroll
@@ -358,7 +361,7 @@ __device__ __forceinline__ void mask_phase(Smem<T, N, HG, SCAN>& sm, int nh, int
         for (int kk = 0; kk < KN; ++kk) {
             const int n = 32 * kk + 8 * g;
             b[kk] = X8{};
-            if (N % 32 == 0 || n < N) b[kk] = ld8(&sm.cs[16 * tb + l16][n]);
+            if (N % 32 == 0 || n < N) b[kk] = lds8<BU>(sm.cs, 16 * tb + l16, n);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -366,48 +369,47 @@ __device__ __forceinline__ void mask_phase(Smem<T, N, HG, SCAN>& sm, int nh, int
         cbt[tb] = acc;
     }
     const int s0 = 16 * SB + 4 * g;
+    const Decay& D = sm.dec[q];
+    const f32x4 fa = *(const f32x4*)&D.fa[s0];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-        if (hh < nh) {
-            const Decay& D = sm.dec[hh];
-            const f32x4 fa = *(const f32x4*)&D.fa[s0];
+    for (int tb = SB + 1; tb < 4; ++tb) {  // off-diagonal: no exponentials
+        const float f = D.fm[tb * (tb - 1) / 2 + SB] * D.fb[16 * tb + l16];
+        X4 v;
 #pragma unroll
-            for (int tb = SB + 1; tb < 4; ++tb) {  // off-diagonal: no exponentials
-                const float f = D.fm[tb * (tb - 1) / 2 + SB] * D.fb[16 * tb + l16];
-                X4 v;
+        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(cbt[tb][i] * (fa[i] * f));
+        *((X4*)&sm.lf[q][lslot(tb, SB >> 1)][lane] + (SB & 1)) = v;
+    }
+    {  // diagonal tile: mask s <= t before the exponential
+        const int t = 16 * SB + l16;
+        const float cst = D.cs2[t];
+        const f32x4 css = *(const f32x4*)&D.cs2[s0];
+        const f32x4 dts = *(const f32x4*)&D.dt[s0];
+        X4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = cvt<T>(cbt[tb][i] * (fa[i] * f));
-                *((X4*)&sm.lf[hh][lslot(tb, SB >> 1)][lane] + (SB & 1)) = v;
-            }
-            {  // diagonal tile: mask s <= t before the exponential
-                const int t = 16 * SB + l16;
-                const float cst = D.cs2[t];
-                const f32x4 css = *(const f32x4*)&D.cs2[s0];
-                const f32x4 dts = *(const f32x4*)&D.dt[s0];
-                X4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool causal = (s0 + i) <= t;
-                    const float e = fexp2(causal ? cst - css[i] : -INFINITY);
-                    v[i] = cvt<T>(causal ? cbt[SB][i] * e * dts[i] : 0.f);
-                }
-                *((X4*)&sm.lf[hh][lslot(SB, SB >> 1)][lane] + (SB & 1)) = v;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const bool causal = (s0 + i) <= t;
+            const float e = fexp2(causal ? cst - css[i] : -INFINITY);
+            v[i] = cvt<T>(causal ? cbt[SB][i] * e * dts[i] : 0.f);
         }
+        *((X4*)&sm.lf[q][lslot(SB, SB >> 1)][lane] + (SB & 1)) = v;
     }
 }
 
-// Two workgroups per CU when their LDS fits in the 160 KB of a gfx950 CU.
+// Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
+// per CU, or one 8-wave one; lighter variants get more from their natural
+// register use.  A scan with state rows wider than 256 bytes gets 512.
 template <typename T, int N, int HG, bool SCAN>
-constexpr int span_occupancy() { return 2 * sizeof(Smem<T, N, HG, SCAN>) <= 160 * 1024 ? 2 : 1; }
+constexpr int span_occupancy() {
+    return HG == 1 && !(SCAN && N * sizeof(T) > 256) ? 2 : 1;
+}
 
 template <typename T, int N, int HG, bool SCAN>
-__global__ __launch_bounds__(kThreads, (span_occupancy<T, N, HG, SCAN>())) void span_kernel(
+__global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) void span_kernel(
     KParams p) {
     using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
-    constexpr int NB = Cf::NB, KN = Cf::KN;
+    constexpr int NB = Cf::NB, KN = Cf::KN, XU = Cf::XU, BU = Cf::BU;
     __shared__ Smem<T, N, HG, SCAN> sm;
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
@@ -450,25 +452,26 @@ __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, HG, SCAN>())) void 
     const int xun = pgw / Cf::EPU;
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
-    const bool active = wave * 16 < pgw;
-    const int pb = pg * kWaves + wave;  // this wave's 16-column block of headdim
+    const int q = wave >> 2, w4 = wave & 3;  // quad = head h0 + q; 16-column block w4
+    const bool active = q < nh && w4 * 16 < pgw;
+    const int pb = pg * kWaves + w4;  // this wave's 16-column block of headdim
+    const int h = h0 + q;
 
-    f32x4 Hs[HG][NB];
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-        const T* sb = (const T*)p.states + (span * p.H + h0 + hh) * (int64_t)p.P * N;
+    f32x4 Hs[NB];
+    {
+        const T* sb = (const T*)p.states + (span * p.H + h) * (int64_t)p.P * N;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            Hs[hh][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (SCAN && active && hh < nh) Hs[hh][nb] = load4(sb + state_off(pb, nb, lane, NB));
+            Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (SCAN && active) Hs[nb] = load4(sb + state_off(pb, nb, lane, NB));
         }
     }
-    float logdec2 = 0.f;  // wave hh: sum of head hh's chunk log2-decays
+    float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
 
     if (SCAN) {
         // mask fragment halves that stay zero: tiles above the diagonal
         // (tb, sb) = (0, 1) and (2, 3)
-        for (int i = tid; i < HG * 2 * 64; i += kThreads) {
+        for (int i = tid; i < HG * 2 * 64; i += Cf::TH) {
             const int hh = i / 128, k = (i / 64) & 1, l = i & 63;
             X4* dst = (X4*)&sm.lf[hh][k ? lslot(2, 1) : lslot(0, 0)][l] + 1;
             *dst = X4{};
@@ -480,20 +483,18 @@ __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, HG, SCAN>())) void 
     cp.len = len;
     cp.reverse = p.reverse;
     cp.j0 = (int64_t)chunk0 * kChunk;
-    cp.clen = (int)imin(kChunk, len - cp.j0);
     const int grp = (int)((int64_t)h0 * p.G / p.H);
-    Stage<T, N, HG, SCAN> st;
-    load_chunk<T, N, HG, SCAN>(st, p, cp, h0, nh, grp, pcol0, xun);
-    T* const yg = (T*)p.y + pcol0 + wave * 16 + 4 * g;
-    const int wc = wave * 16;  // this wave's first column in the X tiles
+    T* const yh = (T*)p.y + pcol0 + w4 * 16 + 4 * g + (int64_t)h * p.ys_h;
+    const int wc = w4 * 16;  // this wave's first column in the X tile
+    const T* xt = sm.xs[q < HG ? q : 0];
 
     for (int c = 0; c < nck; ++c) {
         const bool last_chunk = c + 1 == nck;
         const bool need_update = !SCAN || !last_chunk;
-        __syncthreads();  // previous chunk's tiles are no longer read
-        write_chunk<T, N, HG, SCAN>(sm, st, cp, p.d_init, nh);
-        __syncthreads();
-        ChunkPos nx = cp;
+        cp.j0 = (int64_t)(chunk0 + c) * kChunk;
+        cp.clen = (int)imin(kChunk, len - cp.j0);
+        if (c > 0) __syncthreads();  // previous chunk's tiles are no longer read
+        const float draw = issue_chunk<T, N, HG, SCAN>(sm, p, cp, h0, nh, grp, pcol0, xun);
         int64_t yo[4];
         if (SCAN) {
 #pragma unroll
@@ -502,124 +503,120 @@ __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, HG, SCAN>())) void 
                 yo[tb] = t < cp.clen ? cp.tok(t) * p.ys_t : -1;
             }
         }
-        if (!last_chunk) {
-            nx.j0 = cp.j0 + kChunk;
-            nx.clen = (int)imin(kChunk, len - nx.j0);
-            load_chunk<T, N, HG, SCAN>(st, p, nx, h0, nh, grp, pcol0, xun);
-        }
+        __builtin_amdgcn_s_waitcnt(0);  // this lane's LDS loads and d_raw have landed
+        if (w4 == 0 && q < nh) decay_factors(sm.dec[q], draw, p.d_init, cp.clen, lane);
+        __syncthreads();
 
         if constexpr (SCAN) {
-            // C B^T tiles of s-block `wave`, then every head's masked fragments
-            switch (wave) {
-                case 0: mask_phase<0, T, N, HG, SCAN>(sm, nh, lane); break;
-                case 1: mask_phase<1, T, N, HG, SCAN>(sm, nh, lane); break;
-                case 2: mask_phase<2, T, N, HG, SCAN>(sm, nh, lane); break;
-                default: mask_phase<3, T, N, HG, SCAN>(sm, nh, lane); break;
+            // C B^T tiles of s-block w4, then this quad's head's masked fragments
+            if (q < nh) {
+                switch (w4) {
+                    case 0: mask_phase<0, T, N, HG, SCAN>(sm, q, lane); break;
+                    case 1: mask_phase<1, T, N, HG, SCAN>(sm, q, lane); break;
+                    case 2: mask_phase<2, T, N, HG, SCAN>(sm, q, lane); break;
+                    default: mask_phase<3, T, N, HG, SCAN>(sm, q, lane); break;
+                }
             }
             __syncthreads();
         }
 
         if (active) {
+            const Decay& D = sm.dec[q];
+            if (SCAN) {
+                X8 hf[KN];  // the state as the A operand of H^T C^T
 #pragma unroll
-            for (int hh = 0; hh < HG; ++hh) {
-                if (hh < nh) {
-                    const Decay& D = sm.dec[hh];
-                    const T* xt = &sm.xs[hh][0][0];
-                    if (SCAN) {
-                        const int h = h0 + hh;
-                        X8 hf[KN];  // this head's state as the A operand of H^T C^T
+                for (int kk = 0; kk < KN; ++kk) {
+                    X4 lo, hi = {};
 #pragma unroll
-                        for (int kk = 0; kk < KN; ++kk) {
-                            X4 lo, hi = {};
+                    for (int i = 0; i < 4; ++i) {
+                        lo[i] = cvt<T>(Hs[2 * kk][i]);
+                        if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[2 * kk + 1][i]);
+                    }
+                    hf[kk] = cat<X8, X4>(lo, hi);
+                }
+                // X^T fragments in the K order of the mask tiles:
+                // tokens 32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3)
+                X8 xf[2];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                lo[i] = cvt<T>(Hs[hh][2 * kk][i]);
-                                if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[hh][2 * kk + 1][i]);
-                            }
-                            hf[kk] = cat<X8, X4>(lo, hi);
-                        }
-                        // X^T fragments in the K order of the mask tiles:
-                        // tokens 32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3)
-                        X8 xf[2], lfr[6];
+                for (int kk = 0; kk < 2; ++kk)
+                    xf[kk] = tok_frag<XU>(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, wc, lane);
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-                            xf[kk] = tok_frag(xt, Cf::XP, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, wc,
-                                              lane);
+                for (int th = 0; th < 2; ++th) {  // t-blocks 2*th, 2*th + 1
+                    // every operand of this half first, then the MFMAs
+                    X8 lfa[2], lfb[2], cf[2][KN];
 #pragma unroll
-                        for (int j = 0; j < 6; ++j) lfr[j] = sm.lf[hh][j][lane];
-                        // intra-chunk: y^T += X^T L^T (causal fragments only)
-                        f32x4 yi[4], ye[4];
-                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        yi[0] = mma(xf[0], lfr[lslot(0, 0)], z);
-                        yi[1] = mma(xf[0], lfr[lslot(1, 0)], z);
-                        yi[2] = mma(xf[0], lfr[lslot(2, 0)], z);
-                        yi[3] = mma(xf[0], lfr[lslot(3, 0)], z);
-                        yi[2] = mma(xf[1], lfr[lslot(2, 1)], yi[2]);
-                        yi[3] = mma(xf[1], lfr[lslot(3, 1)], yi[3]);
-                        // inter-chunk: y^T += H^T C^T, four independent chains
+                    for (int j = 0; j < 2; ++j) {
+                        lfa[j] = sm.lf[q][lslot(2 * th + j, 0)][lane];
+                        if (th == 1) lfb[j] = sm.lf[q][lslot(2 + j, 1)][lane];
+                    }
 #pragma unroll
-                        for (int tb = 0; tb < 4; ++tb) ye[tb] = z;
+                    for (int kk = 0; kk < KN; ++kk) {
+                        const int n0 = 32 * kk + 4 * g, n1 = n0 + 16;
 #pragma unroll
-                        for (int kk = 0; kk < KN; ++kk) {
-                            const int n0 = 32 * kk + 4 * g, n1 = n0 + 16;
-                            X8 cf[4];
-#pragma unroll
-                            for (int tb = 0; tb < 4; ++tb) {
-                                X4 c0 = {}, c1 = {};
-                                if (N % 32 == 0 || n0 < N) c0 = ld4(&sm.cs[16 * tb + l16][n0]);
-                                if (N % 32 == 0 || n1 < N) c1 = ld4(&sm.cs[16 * tb + l16][n1]);
-                                cf[tb] = cat<X8, X4>(c0, c1);
-                            }
-#pragma unroll
-                            for (int tb = 0; tb < 4; ++tb) ye[tb] = mma(hf[kk], cf[tb], ye[tb]);
-                        }
-                        T* const yh = yg + (int64_t)h * p.ys_h;
-#pragma unroll
-                        for (int tb = 0; tb < 4; ++tb) {
-                            const float sc = D.fe[16 * tb + l16];
-                            f32x4 o;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) o[i] = yi[tb][i] + sc * ye[tb][i];
-                            if (yo[tb] >= 0) store4(yh + yo[tb], o);
+                        for (int j = 0; j < 2; ++j) {
+                            const int t = 16 * (2 * th + j) + l16;
+                            X4 c0 = {}, c1 = {};
+                            if (N % 32 == 0 || n0 < N) c0 = lds4<BU>(sm.cs, t, n0);
+                            if (N % 32 == 0 || n1 < N) c1 = lds4<BU>(sm.cs, t, n1);
+                            cf[j][kk] = cat<X8, X4>(c0, c1);
                         }
                     }
-                    if (need_update) {
-                        // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
-                        const float decay = D.fe[kChunk - 1];
+                    // intra-chunk: y^T += X^T L^T (causal fragments only)
+                    f32x4 yi[2], ye[2];
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) Hs[hh][nb] *= decay;
+                    for (int j = 0; j < 2; ++j) {
+                        yi[j] = mma(xf[0], lfa[j], z);
+                        if (th == 1) yi[j] = mma(xf[1], lfb[j], yi[j]);
+                    }
+                    // inter-chunk: y^T += H^T C^T, two independent chains
+                    ye[0] = z;
+                    ye[1] = z;
 #pragma unroll
-                        for (int kk = 0; kk < kChunk / 32; ++kk) {
-                            const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
-                            const f32x8 ws = ld8(&D.w[s0]);
-                            const X8 xv = tok_frag(xt, Cf::XP, s0, s0 + 4, wc, lane);
-                            X8 b, bt[NB];
+                    for (int kk = 0; kk < KN; ++kk)
 #pragma unroll
-                            for (int nb = 0; nb < NB; ++nb)
-                                bt[nb] = tok_frag(&sm.bs[0][0], Cf::NP, s0, s0 + 4, 16 * nb, lane);
+                        for (int j = 0; j < 2; ++j) ye[j] = mma(hf[kk], cf[j][kk], ye[j]);
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
+                    for (int j = 0; j < 2; ++j) {
+                        const int tb = 2 * th + j;
+                        const float sc = D.fe[16 * tb + l16];
+                        f32x4 o;
 #pragma unroll
-                            for (int nb = 0; nb < NB; ++nb) Hs[hh][nb] = mma(bt[nb], b, Hs[hh][nb]);
-                        }
+                        for (int i = 0; i < 4; ++i) o[i] = yi[j][i] + sc * ye[j][i];
+                        if (yo[tb] >= 0) store4(yh + yo[tb], o);
                     }
                 }
             }
+            if (need_update) {
+                // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
+                const float decay = D.fe[kChunk - 1];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) Hs[nb] *= decay;
+#pragma unroll
+                for (int kk = 0; kk < kChunk / 32; ++kk) {
+                    const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
+                    const f32x8 ws = ld8(&D.w[s0]);
+                    const X8 xv = tok_frag<XU>(xt, s0, s0 + 4, wc, lane);
+                    X8 b, bt[NB];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bt[nb] = tok_frag<BU>(sm.bs, s0, s0 + 4, 16 * nb, lane);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) Hs[nb] = mma(bt[nb], b, Hs[nb]);
+                }
+            }
         }
-        if (!SCAN && wave < nh) logdec2 += sm.dec[wave].cs2[kChunk - 1];
-        cp = nx;
+        if (!SCAN && w4 == 0 && q < nh) logdec2 += sm.dec[q].cs2[kChunk - 1];
     }
 
     if (!SCAN) {
+        if (active) {
+            T* sb = (T*)p.states + (span * p.H + h) * (int64_t)p.P * N;
 #pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-            if (hh < nh && active) {
-                T* sb = (T*)p.states + (span * p.H + h0 + hh) * (int64_t)p.P * N;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) store4(sb + state_off(pb, nb, lane, NB), Hs[hh][nb]);
-            }
+            for (int nb = 0; nb < NB; ++nb) store4(sb + state_off(pb, nb, lane, NB), Hs[nb]);
         }
-        if (pg == 0 && wave < nh && lane == 0) p.decay[span * p.H + h0 + wave] = fexp2(logdec2);
+        if (pg == 0 && w4 == 0 && q < nh && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
     }
 }
 
@@ -763,7 +760,7 @@ hipError_t launch_span_hg(const KParams& p, int hg, hipStream_t s) {
     if (nreal == 0) return hipSuccess;
     const int64_t per = (nreal + kXcds - 1) / kXcds;
     hipLaunchKernelGGL((span_kernel<T, N, HG, SCAN>), dim3((unsigned)(per * kXcds)),
-                       dim3(kThreads), 0, s, p);
+                       dim3(kThreads * HG), 0, s, p);
     return hipGetLastError();
 }
 
@@ -771,11 +768,10 @@ hipError_t launch_span_hg(const KParams& p, int hg, hipStream_t s) {
 // can carry at this d_state.
 template <typename T, int N, bool SCAN>
 hipError_t launch_span_t(const KParams& p, hipStream_t s) {
-    constexpr int MAXH = SCAN ? heads_scan(N) : heads_state(N);
+    constexpr int MAXH = SCAN ? heads_scan(N, sizeof(T)) : heads_state(N, sizeof(T));
     const int hg = SCAN ? p.hg_scan : p.hg_state;
     if (hg == 1) return launch_span_hg<T, N, 1, SCAN>(p, 1, s);
     if (hg == 2 && MAXH >= 2) return launch_span_hg<T, N, (MAXH >= 2 ? 2 : 1), SCAN>(p, 2, s);
-    if (hg == 4 && MAXH >= 4) return launch_span_hg<T, N, (MAXH >= 4 ? 4 : 1), SCAN>(p, 4, s);
     return hipErrorInvalidValue;
 }
 
@@ -802,12 +798,15 @@ hipError_t launch_span(const KParams& p, int dtype, int N, hipStream_t s) {
 
 }  // namespace
 
-int span_max_heads(int N, bool scan) { return scan ? heads_scan(N) : heads_state(N); }
+int span_max_heads(int dtype, int N, bool scan) {
+    const int esz = dtype == 1 ? 2 : 4;
+    return scan ? heads_scan(N, esz) : heads_state(N, esz);
+}
 
 size_t span_lds_bytes(int dtype, int N, bool scan) {
 #define SSD_LDS(T, NN)                                                 \
-    (scan ? sizeof(Smem<T, NN, heads_scan(NN), true>)                  \
-          : sizeof(Smem<T, NN, heads_state(NN), false>))
+    (scan ? sizeof(Smem<T, NN, heads_scan(NN, sizeof(T)), true>)       \
+          : sizeof(Smem<T, NN, heads_state(NN, sizeof(T)), false>))
     if (dtype == 1) {
         switch (N) {
             case 16: return SSD_LDS(bf16, 16);
