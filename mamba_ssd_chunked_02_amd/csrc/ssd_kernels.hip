@@ -87,10 +87,6 @@ __device__ __forceinline__ X8 cat(const X4& a, const X4& b) {
     return r;
 }
 
-__device__ __forceinline__ float softplus(float z) {
-    return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
-}
-
 template <typename T>
 __device__ __forceinline__ T cvt(float v) { return (T)v; }
 
@@ -104,6 +100,24 @@ __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
     *(bf16x4*)p = o;
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& v) { *(f32x4*)p = v; }
+
+// The same stores issued as inline assembly.  The compiler's wait insertion
+// treats pending stores and loads on the vector-memory counter as unordered
+// and would then wait for every outstanding load (the prefetched tiles
+// included) before the next use of a loaded register; stores it does not see
+// leave its waits for loads exact.  Loads still retire in issue order, so
+// every wait it computes stays sufficient.  The s_nop covers the one wait
+// state a store of more than 8 bytes needs before its data registers are
+// overwritten.
+__device__ __forceinline__ void store4_async(bf16* p, const f32x4& v) {
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (bf16)v[i];
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(o) : "memory");
+}
+__device__ __forceinline__ void store4_async(float* p, const f32x4& v) {
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 0" ::"v"(p), "v"(v) : "memory");
+}
 
 // Four consecutive span-state values (states are stored in the input type).
 __device__ __forceinline__ f32x4 load4(const bf16* p) {
@@ -129,7 +143,7 @@ struct Cfg {
 // Heads (quads) per workgroup: up to 2 (8 waves), one for the scan when a
 // state row is wider than 256 bytes (its per-wave registers exceed 256).
 constexpr int heads_state(int N, int esz) { return 2; }
-constexpr int heads_scan(int N, int esz) { return N * esz <= 256 ? 2 : 1; }
+constexpr int heads_scan(int N, int esz) { return N * esz <= (esz == 2 ? 256 : 128) ? 2 : 1; }
 
 // Wave index within the workgroup as a scalar, so branches on it stay uniform.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -157,77 +171,127 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 // Raw v_exp_f32: every argument here is <= 0, results below 2^-126 flush to 0.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS tiles are 64 token rows of U 16-byte units, unpadded; unit u of row r
-// sits at unit u ^ (r & M) (M = min(U, 8) - 1), which spreads the 16-row
-// column reads of the MFMA operands over all banks.  swz() gives the element
-// offset of (row r, column e).
-template <int U, int EPU>
-__device__ __forceinline__ int swz(int r, int e) {
-    constexpr int M = (U < 8 ? U : 8) - 1;
-    return r * (U * EPU) + (((e / EPU) ^ (r & M)) * EPU) + (e % EPU);
+// softplus(z) = max(z, 0) + log(1 + e^{-|z|}) from the hardware exp2 / log2.
+// Below v = e^{-|z|} = 1/64, where 1 + v would drop v's low bits, log(1 + v)
+// is its alternating series to v^4 (relative error under v^4 / 5 < 1e-8).
+__device__ __forceinline__ float softplus(float z) {
+    constexpr float kLn2 = 0.69314718055994531f;
+    const float v = fexp2(-fabsf(z) * kLog2e);
+    const float series = v * (1.f - v * (0.5f - v * (1.f / 3.f - v * 0.25f)));
+    const float direct = __builtin_amdgcn_logf(1.f + v) * kLn2;
+    return fmaxf(z, 0.f) + (v < 0.015625f ? series : direct);
 }
 
-// Issue the direct global -> LDS loads (global_load_lds_dwordx4) of one tile:
-// instruction i fills physical units 64i .. 64i+63, lane l the unit 64i + l.
-// Rows past the chunk read row 0 and columns past `ucols` read unit 0: such
-// entries only ever meet zero weights.  `rowp(r)` is the global row pointer.
-template <int U, int EPU, typename T, typename RowPtr>
-__device__ __forceinline__ void issue_tile(T* tile, int first, int step, int clen, int ucols,
-                                           int lane, RowPtr rowp) {
-    constexpr int M = (U < 8 ? U : 8) - 1;
+// LDS tiles are column-blocked: 16-column blocks of 64 token rows, block b
+// at element offset b * 1024 (2 KB for bf16, 4 KB for fp32).  Within a block
+// row r is stored at row r ^ (4 * bit3(r)) and its 16-byte units are XORed
+// with bit3(r).  With that, every LDS read pattern used here touches distinct
+// banks: 16 consecutive rows of one unit (C B^T operands), and 4-row groups
+// 8 rows apart of the transposing reads; and the offset of block b is a
+// constant, so the fragments of all blocks share one address register.
+template <typename T>
+__device__ __forceinline__ int boff(int r, int blk, int ec) {
+    constexpr int EPU = 16 / sizeof(T);  // elements per 16-byte unit
+    const int b3 = (r >> 3) & 1;
+    const int pr = r ^ (b3 << 2);
+    const int u = (ec / EPU) ^ b3;
+    return blk * (kChunk * 16) + pr * 16 + u * EPU + ec % EPU;
+}
+
+// Issue the direct global -> LDS loads (global_load_lds_dwordx4) of
+// instructions first + k*STEP (k < NI) of a column-blocked tile: instruction
+// i fills the 1 KB at i KB, lane l its 16 bytes at l*16.  Tile row r is the
+// global row at row0 + r * rstride (elements; negative for an anti-causal
+// pass), column c at row + c.  Rows at or past clen read row 0 and columns at
+// or past ccols read column 0: such entries only ever meet zero weights or
+// are never read.  The per-lane offsets do not depend on the chunk, so the
+// compiler keeps them out of the chunk loop; a full chunk needs no clamp.
+template <int NI, int STEP, int NINST, typename T>
+__device__ __forceinline__ void issue_tile(T* __restrict__ tile, const T* row0, int rstride,
+                                           int first, int clen, int ccols, int lane) {
+    constexpr int EPU = 16 / sizeof(T), W = 16 / EPU;  // units per block row
+    const bool full = clen == kChunk;
 #pragma unroll
-    for (int i = first; i < U; i += step) {
-        const int pu = 64 * i + lane;
-        const int r = pu / U;
-        int u = (pu % U) ^ (r & M);
-        if (u >= ucols) u = 0;
-        const T* g = rowp(r < clen ? r : 0) + u * EPU;
+    for (int k = 0; k < NI; ++k) {
+        const int i = first + k * STEP;
+        if (NINST % STEP != 0 && i >= NINST) break;
+        const int j = (i % W) * 64 + lane;   // unit within the block
+        const int pr = j / W, pu = j % W;    // stored row and unit
+        const int b3 = (pr >> 3) & 1;
+        const int r = pr ^ (b3 << 2);        // logical row
+        int col = (i / W) * 16 + (pu ^ b3) * EPU;
+        if (col >= ccols) col = 0;
+        const int off = r * rstride + col;
+        const T* g = row0 + (full || r < clen ? off : col);
         __builtin_amdgcn_global_load_lds((const void*)g,
-                                         (__attribute__((address_space(3))) void*)(tile + 64 * i * EPU),
+                                         (__attribute__((address_space(3))) void*)(tile + i * 64 * EPU),
                                          16, 0, 0);
     }
 }
 
-// 8 / 4 consecutive elements of a swizzled tile (e a multiple of 8 / 4).
-template <int U>
-__device__ __forceinline__ bf16x8 lds8(const bf16* t, int r, int e) { return ld8(t + swz<U, 8>(r, e)); }
-template <int U>
-__device__ __forceinline__ f32x8 lds8(const float* t, int r, int e) {
-    return cat<f32x8, f32x4>(ld4(t + swz<U, 4>(r, e)), ld4(t + swz<U, 4>(r, e + 4)));
+// Wait until at most NOUT vector-memory operations of this wave are in
+// flight (they retire in issue order).  A compiler builtin, so the compiler
+// knows about the wait and does not repeat it.
+template <int NOUT>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(NOUT >= 0 && NOUT < 64, "vm_wait");
+    // vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima
+    __builtin_amdgcn_s_waitcnt((NOUT & 15) | ((NOUT >> 4) << 14) | 0x0F70);
 }
-template <int U>
-__device__ __forceinline__ bf16x4 lds4(const bf16* t, int r, int e) { return ld4(t + swz<U, 8>(r, e)); }
-template <int U>
-__device__ __forceinline__ f32x4 lds4(const float* t, int r, int e) { return ld4(t + swz<U, 4>(r, e)); }
+// Workgroup barrier after this wave's own LDS operations have completed; the
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-// Token-contracted MFMA fragment from a swizzled [token][col] tile: this
-// lane's column c0 + lane%16 at tokens r0..r0+3 (slots 0-3) and r1..r1+3
-// (slots 4-7); r0, r1 are the same for the 16 lanes of a group.  bf16 uses
-// the gfx950 transposing read (ds_read_b64_tr_b16): lane i of a 16-lane
-// group receives, in slot k, element i%4 of the 8 bytes addressed by lane
-// 4k + i/4 of the group, so lane j addresses row r + j/4, columns
-// c0 + 4(j%4)..+3.
+// 4 consecutive elements (8 or 16 bytes) at (row r, block blk, column ec) of
+// a column-blocked tile; ec a multiple of 4.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x4 tld4(const T* t, int r, int blk, int ec) {
+    return ld4(t + boff<T>(r, blk, ec));
+}
+
+// Token-contracted MFMA fragment of block blk of a column-blocked tile: lane
+// (l16, g) gets column 16*blk + l16 at tokens r0..r0+3 (slots 0-3) and
+// r1..r1+3 (slots 4-7); r0, r1 are the same for the 16 lanes of a group.
+// bf16 uses the gfx950 transposing read (ds_read_b64_tr_b16): lane i of a
+// 16-lane group receives, in slot k, element i%4 of the 8 bytes addressed by
+// lane 4k + i/4 of the group, so lane j addresses row r + j/4, columns
+// 4*(j%4) .. +3 of the block.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x4 ldtr(const bf16* p) {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
-template <int U>
-__device__ __forceinline__ bf16x8 tok_frag(const bf16* t, int r0, int r1, int c0, int lane) {
-    const int j = lane & 15, dr = j >> 2, e = c0 + 4 * (j & 3);
-    return cat<bf16x8, bf16x4>(ldtr(t + swz<U, 8>(r0 + dr, e)), ldtr(t + swz<U, 8>(r1 + dr, e)));
+__device__ __forceinline__ bf16x8 tok_frag(const bf16* t, int r0, int r1, int blk, int lane) {
+    const int j = lane & 15, dr = j >> 2, ec = 4 * (j & 3);
+    return cat<bf16x8, bf16x4>(ldtr(t + boff<bf16>(r0 + dr, blk, ec)),
+                               ldtr(t + boff<bf16>(r1 + dr, blk, ec)));
 }
-template <int U>
-__device__ __forceinline__ f32x8 tok_frag(const float* t, int r0, int r1, int c0, int lane) {
-    const int e = c0 + (lane & 15);
+__device__ __forceinline__ f32x8 tok_frag(const float* t, int r0, int r1, int blk, int lane) {
+    const int ec = lane & 15;
     f32x8 v;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        v[k] = t[swz<U, 4>(r0 + k, e)];
-        v[4 + k] = t[swz<U, 4>(r1 + k, e)];
+        v[k] = t[boff<float>(r0 + k, blk, ec)];
+        v[4 + k] = t[boff<float>(r1 + k, blk, ec)];
     }
     return v;
+}
+
+// Operand fragment over the state dimension (K = n) of tile row r for the K
+// step kk: a lane of group g holds n = 32kk + 4g + (0..3) in slots 0-3 and
+// n = 32kk + 16 + 4g + (0..3) in slots 4-7 (zeros past N).  This is the K
+// order of a pair of state result tiles (rows 4g..4g+3 of blocks 2kk and
+// 2kk+1), so the state feeds H^T C^T with no data movement.
+template <int N, typename T>
+__device__ __forceinline__ typename Vec<T>::x8 tile_frag(const T* tile, int r, int kk, int g) {
+    using X4 = typename Vec<T>::x4;
+    const X4 lo = tld4(tile, r, 2 * kk, 4 * g);
+    X4 hi = {};
+    if (N % 32 == 0 || 2 * kk + 1 < N / 16) hi = tld4(tile, r, 2 * kk + 1, 4 * g);
+    return cat<typename Vec<T>::x8, X4>(lo, hi);
 }
 
 // Per-head, per-chunk decay factors (cs = within-chunk cumulative -d in log2
@@ -260,61 +324,27 @@ __device__ __forceinline__ int64_t state_off(int pb, int nb, int lane, int NB) {
     return ((int64_t)(pb * NB + nb) * 64 + lane) * 4;
 }
 
-// LDS of one span workgroup.
+// LDS of one span workgroup.  X and B tiles and the decay factors are
+// double-buffered: chunk c+1's fill one buffer while chunk c is computed
+// from the other; d_raw arrives two chunks ahead (three buffers).  The C
+// tile has one buffer, refilled as soon as the step's C reads are done.
 template <typename T, int N, int HG, bool SCAN>
 struct __attribute__((aligned(16))) Smem {
-    using C = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
-    T xs[HG][kChunk * kPGroup];        // X of every head, this group's 64 columns
-    T bs[kChunk * N];                  // B
-    T cs[SCAN ? kChunk * N : 1];       // C                               (scan only)
-    X8 lf[SCAN ? HG : 1][6][64];       // masked C B^T fragments per head (scan only)
-    Decay dec[HG];
+    T xs[2][HG][kChunk * kPGroup];      // X of every head, this group's 64 columns
+    T bs[2][kChunk * N];                // B
+    T cs[SCAN ? kChunk * N : 1];        // C (scan)
+    X8 lf[SCAN ? HG : 1][SCAN ? 6 : 1][SCAN ? 64 : 1];  // masked C B^T per head (scan)
+    Decay dec[2][HG];                   // per head
+    uint32_t dr[3][HG][kChunk];         // d_raw per head, one token per lane
 };
 
-struct ChunkPos {
-    int64_t start, len, j0;  // sequence start/length, first logical token
-    int clen;                // tokens of this chunk (<= 64)
-    int reverse;
-    __device__ __forceinline__ int64_t tok(int s) const {
-        const int64_t j = j0 + s;
-        return start + (reverse ? (len - 1 - j) : j);
-    }
-};
-
-// Issue every global load of one chunk: quad q's X tile (head h0 + q) and
-// all of B / C straight into LDS; the first wave of each quad also loads its
-// head's d_raw, one token per lane, into a register.
-template <typename T, int N, int HG, bool SCAN>
-__device__ __forceinline__ float issue_chunk(Smem<T, N, HG, SCAN>& sm, const KParams& p,
-                                             const ChunkPos& cp, int h0, int nh, int grp,
-                                             int pcol0, int xun) {
-    using C = Cfg<T, N, HG>;
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int q = wave >> 2, w4 = wave & 3;
-    const int64_t HP = (int64_t)p.H * p.P, GN = (int64_t)p.G * N;
-    if (q < nh) {
-        const T* xh = (const T*)p.x + (int64_t)(h0 + q) * p.P + pcol0;
-        issue_tile<C::XU, C::EPU>(sm.xs[q], w4, 4, cp.clen, xun, lane,
-                                  [&](int r) { return xh + cp.tok(r) * HP; });
-    }
-    const T* bg = (const T*)p.B + (int64_t)grp * N;
-    issue_tile<C::BU, C::EPU>(sm.bs, wave, C::NW, cp.clen, C::BU, lane,
-                              [&](int r) { return bg + cp.tok(r) * GN; });
-    if (SCAN) {
-        const T* cg = (const T*)p.C + (int64_t)grp * N;
-        issue_tile<C::BU, C::EPU>(sm.cs, wave, C::NW, cp.clen, C::BU, lane,
-                                  [&](int r) { return cg + cp.tok(r) * GN; });
-    }
-    float v = 0.f;
-    if (w4 == 0 && q < nh && lane < cp.clen)
-        v = (float)((const T*)p.d_raw)[cp.tok(lane) * p.H + h0 + q];
-    return v;
-}
-
-// The first wave of quad q forms head h0 + q's decay factors.
-__device__ __forceinline__ void decay_factors(Decay& D, float draw, float d_init, int clen,
+// One wave forms a head's decay factors from d_raw as loaded into LDS (a
+// bf16 value sits in the low half of its 32-bit slot).
+template <typename T>
+__device__ __forceinline__ void decay_factors(Decay& D, uint32_t raw, float d_init, int clen,
                                               int lane) {
+    const float draw = __uint_as_float(sizeof(T) == 2 ? raw << 16 : raw);
     const float dt = lane < clen ? softplus(draw + d_init) : 0.f;
     const float v = wave_prefix_sum(-dt * kLog2e);
     const float c1 = lane_value(v, 15), c2 = lane_value(v, 31);
@@ -336,63 +366,39 @@ __device__ __forceinline__ void decay_factors(Decay& D, float draw, float d_init
     }
 }
 
-// C B^T tiles of s-block SB (t-blocks tb >= SB: row s = 16*SB + 4g + i,
-// column t = 16*tb + l16 of the MFMA result), times head q's decay mask,
-// rounded, as halves of q's intra-chunk B fragments.
-template <int SB, typename T, int N, int HG, bool SCAN>
-__device__ __forceinline__ void mask_phase(Smem<T, N, HG, SCAN>& sm, int q, int lane) {
-    using Cf = Cfg<T, N, HG>;
-    using X8 = typename Vec<T>::x8;
+// One 16x16 tile (t-block TB, s-block SB) of C B^T for head q: rows
+// s = 16*SB + 4g + i, column t = 16*TB + l16 of the MFMA result, times the
+// head's decay mask, rounded, written as half SB&1 of q's fragment slot.
+template <int TB, int SB, typename T, int N, int HG, bool SCAN>
+__device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay& D, int q,
+                                          int lane,
+                                          const typename Vec<T>::x8 (&bf)[Cfg<T, N, HG>::KN],
+                                          const typename Vec<T>::x8 (&cf)[Cfg<T, N, HG>::KN]) {
     using X4 = typename Vec<T>::x4;
-    constexpr int KN = Cf::KN, BU = Cf::BU;
-    const int l16 = lane & 15, g = lane >> 4;
-    X8 a[KN];  // B rows 16*SB + l16, n = 32kk + 8g ..
+    constexpr int KN = Cfg<T, N, HG>::KN;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk) {
-        const int n = 32 * kk + 8 * g;
-        a[kk] = X8{};
-        if (N % 32 == 0 || n < N) a[kk] = lds8<BU>(sm.bs, 16 * SB + l16, n);
-    }
-    f32x4 cbt[4];
+    for (int kk = 0; kk < KN; ++kk) acc = mma(bf[kk], cf[kk], acc);
+    const int l16 = lane & 15, s0 = 16 * SB + 4 * (lane >> 4);
+    X4 v;
+    if constexpr (TB > SB) {  // off-diagonal: no exponentials
+        const f32x4 fa = *(const f32x4*)&D.fa[s0];
+        const float f = D.fm[TB * (TB - 1) / 2 + SB] * D.fb[16 * TB + l16];
 #pragma unroll
-    for (int tb = SB; tb < 4; ++tb) {
-        X8 b[KN];
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) {
-            const int n = 32 * kk + 8 * g;
-            b[kk] = X8{};
-            if (N % 32 == 0 || n < N) b[kk] = lds8<BU>(sm.cs, 16 * tb + l16, n);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) acc = mma(a[kk], b[kk], acc);
-        cbt[tb] = acc;
-    }
-    const int s0 = 16 * SB + 4 * g;
-    const Decay& D = sm.dec[q];
-    const f32x4 fa = *(const f32x4*)&D.fa[s0];
-#pragma unroll
-    for (int tb = SB + 1; tb < 4; ++tb) {  // off-diagonal: no exponentials
-        const float f = D.fm[tb * (tb - 1) / 2 + SB] * D.fb[16 * tb + l16];
-        X4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(cbt[tb][i] * (fa[i] * f));
-        *((X4*)&sm.lf[q][lslot(tb, SB >> 1)][lane] + (SB & 1)) = v;
-    }
-    {  // diagonal tile: mask s <= t before the exponential
-        const int t = 16 * SB + l16;
+        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(acc[i] * (fa[i] * f));
+    } else {  // diagonal: mask s <= t before the exponential
+        const int t = 16 * TB + l16;
         const float cst = D.cs2[t];
         const f32x4 css = *(const f32x4*)&D.cs2[s0];
         const f32x4 dts = *(const f32x4*)&D.dt[s0];
-        X4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool causal = (s0 + i) <= t;
             const float e = fexp2(causal ? cst - css[i] : -INFINITY);
-            v[i] = cvt<T>(causal ? cbt[SB][i] * e * dts[i] : 0.f);
+            v[i] = cvt<T>(causal ? acc[i] * e * dts[i] : 0.f);
         }
-        *((X4*)&sm.lf[q][lslot(SB, SB >> 1)][lane] + (SB & 1)) = v;
     }
+    if constexpr (SCAN) *((X4*)&sm.lf[q][lslot(TB, SB >> 1)][lane] + (SB & 1)) = v;
 }
 
 // Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
@@ -409,7 +415,10 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
-    constexpr int NB = Cf::NB, KN = Cf::KN, XU = Cf::XU, BU = Cf::BU;
+    constexpr int NB = Cf::NB, KN = Cf::KN, EPU = Cf::EPU;
+    constexpr int W = 16 / EPU;               // 16-byte units per block row
+    constexpr int XI = 4 * W, BI = NB * W;    // load instructions per X / B / C tile
+    constexpr int DW = 3;                     // wave of each quad that forms the decay
     __shared__ Smem<T, N, HG, SCAN> sm;
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
@@ -449,13 +458,53 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
 
     const int pcol0 = pg * kPGroup;
     const int pgw = min(kPGroup, p.P - pcol0);
-    const int xun = pgw / Cf::EPU;
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
     const int q = wave >> 2, w4 = wave & 3;  // quad = head h0 + q; 16-column block w4
-    const bool active = q < nh && w4 * 16 < pgw;
+    const bool live = q < nh;                // this quad has a head
+    const bool active = live && w4 * 16 < pgw;  // this wave's results are stored
     const int pb = pg * kWaves + w4;  // this wave's 16-column block of headdim
     const int h = h0 + q;
+
+    // Token of row r of chunk c: tok0(c) + dir * r.
+    const int dir = p.reverse ? -1 : 1;
+    const int HP = p.H * p.P, GN = p.G * N;
+    const int grp = (int)((int64_t)h0 * p.G / p.H);
+    // Every wave computes, with a valid head even in a quad without one or
+    // past the headdim; only active waves store what they computed.
+    const int hc = live ? h : h0;
+    const T* const xg = (const T*)p.x + (int64_t)hc * p.P + pcol0;
+    const T* const bg = (const T*)p.B + (int64_t)grp * N;
+    const T* const cg = (const T*)p.C + (int64_t)grp * N;
+    const T* const dg = (const T*)p.d_raw + hc;
+    auto tok0 = [&](int c) -> int64_t {
+        const int64_t j0 = (int64_t)(chunk0 + c) * kChunk;
+        return start + (p.reverse ? len - 1 - j0 : j0);
+    };
+    auto clen_of = [&](int c) -> int { return (int)imin(kChunk, len - (int64_t)(chunk0 + c) * kChunk); };
+    // Chunk c's X tile (wave w4 loads its own 16-column block) and this
+    // wave's share of the B tile.
+    auto issue_xb = [&](int c, T* __restrict__ xdst, T* __restrict__ bdst) {
+        const int64_t t0 = tok0(c);
+        const int cl = clen_of(c);
+        issue_tile<W, 1, XI>(xdst, xg + t0 * HP, dir * HP, w4 * W, cl, pgw, lane);
+        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bg + t0 * GN, dir * GN, wave, cl, N,
+                                                        lane);
+    };
+    // This wave's share of chunk c's C tile (scan).
+    auto issue_c = [&](int c, T* __restrict__ cdst) {
+        if constexpr (SCAN)
+            issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cg + tok0(c) * GN, dir * GN, wave,
+                                                            clen_of(c), N, lane);
+    };
+    // The quad head's d_raw of chunk c, one token per lane (decay wave only).
+    auto issue_d = [&](int c, uint32_t* __restrict__ ddst) {
+        const int cl = clen_of(c);
+        const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * p.H);
+        auto* lds = (__attribute__((address_space(3))) void*)ddst;
+        if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
+        else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+    };
 
     f32x4 Hs[NB];
     {
@@ -468,7 +517,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     }
     float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
 
-    if (SCAN) {
+    if constexpr (SCAN) {
         // mask fragment halves that stay zero: tiles above the diagonal
         // (tb, sb) = (0, 1) and (2, 3)
         for (int i = tid; i < HG * 2 * 64; i += Cf::TH) {
@@ -478,116 +527,143 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
         }
     }
 
-    ChunkPos cp;
-    cp.start = start;
-    cp.len = len;
-    cp.reverse = p.reverse;
-    cp.j0 = (int64_t)chunk0 * kChunk;
-    const int grp = (int)((int64_t)h0 * p.G / p.H);
     T* const yh = (T*)p.y + pcol0 + w4 * 16 + 4 * g + (int64_t)h * p.ys_h;
-    const int wc = w4 * 16;  // this wave's first column in the X tile
-    const T* xt = sm.xs[q < HG ? q : 0];
+
+    // Software pipeline over the span's chunks; step c:
+    //   wait for chunk c's tiles; barrier; issue chunk c+1's X and B tiles
+    //   and chunk c+2's d_raw into the free buffers; (scan) the inter-chunk
+    //   term H^T C^T and the masked C B^T; the decay wave forms chunk c+1's
+    //   decay factors; (scan) barrier, issue chunk c+1's C tile, write y;
+    //   advance the state.
+    // Only loads into LDS are in flight across a step, and the explicit wait
+    // at its top covers them; the compiler itself never waits for them (the
+    // restrict qualifiers below tell it that the step's LDS reads and the
+    // loads it issues touch different buffers).
+    if (w4 == DW) {
+        issue_d(0, sm.dr[0][q]);
+        if (nck > 1) issue_d(1, sm.dr[1][q]);
+    }
+    issue_xb(0, sm.xs[0][q], sm.bs[0]);
+    issue_c(0, sm.cs);
+    vm_wait<0>();
+    if (w4 == DW) decay_factors<T>(sm.dec[0][q], sm.dr[0][q][lane], p.d_init, clen_of(0), lane);
 
     for (int c = 0; c < nck; ++c) {
-        const bool last_chunk = c + 1 == nck;
-        const bool need_update = !SCAN || !last_chunk;
-        cp.j0 = (int64_t)(chunk0 + c) * kChunk;
-        cp.clen = (int)imin(kChunk, len - cp.j0);
-        if (c > 0) __syncthreads();  // previous chunk's tiles are no longer read
-        const float draw = issue_chunk<T, N, HG, SCAN>(sm, p, cp, h0, nh, grp, pcol0, xun);
-        int64_t yo[4];
-        if (SCAN) {
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const int t = 16 * tb + l16;
-                yo[tb] = t < cp.clen ? cp.tok(t) * p.ys_t : -1;
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // this lane's LDS loads and d_raw have landed
-        if (w4 == 0 && q < nh) decay_factors(sm.dec[q], draw, p.d_init, cp.clen, lane);
-        __syncthreads();
+        const bool last = c + 1 == nck;
+        const int buf = c & 1;
+        const int cl = clen_of(c);
+        const int64_t t0 = tok0(c);
+        const Decay& D = sm.dec[buf][q];
 
-        if constexpr (SCAN) {
-            // C B^T tiles of s-block w4, then this quad's head's masked fragments
-            if (q < nh) {
-                switch (w4) {
-                    case 0: mask_phase<0, T, N, HG, SCAN>(sm, q, lane); break;
-                    case 1: mask_phase<1, T, N, HG, SCAN>(sm, q, lane); break;
-                    case 2: mask_phase<2, T, N, HG, SCAN>(sm, q, lane); break;
-                    default: mask_phase<3, T, N, HG, SCAN>(sm, q, lane); break;
-                }
-            }
-            __syncthreads();
-        }
+        // After chunk c's loads this wave issued, in an active scan wave,
+        // exactly four y stores (the previous chunk is full), else nothing.
+        if (SCAN && active && c > 0) vm_wait<4>();
+        else vm_wait<0>();
+        block_sync();  // every wave's loads of chunk c and its decay factors are in LDS
 
-        if (active) {
-            const Decay& D = sm.dec[q];
-            if (SCAN) {
-                X8 hf[KN];  // the state as the A operand of H^T C^T
+        auto body = [&](const T* __restrict__ xt, const T* __restrict__ bt_tile,
+                        const T* __restrict__ ct, const uint32_t* __restrict__ dnext,
+                        T* __restrict__ xn, T* __restrict__ bn, T* __restrict__ cn,
+                        uint32_t* __restrict__ dn2, Decay* __restrict__ decn) {
+            if (!last) {
+                issue_xb(c + 1, xn, bn);
+                if (w4 == DW && c + 2 < nck) issue_d(c + 2, dn2);
+            }
+
+            if constexpr (SCAN) {
+                // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
+                X8 cf[4][KN];
 #pragma unroll
-                for (int kk = 0; kk < KN; ++kk) {
-                    X4 lo, hi = {};
+                for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        lo[i] = cvt<T>(Hs[2 * kk][i]);
-                        if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[2 * kk + 1][i]);
+                    for (int kk = 0; kk < KN; ++kk) cf[tb][kk] = tile_frag<N>(ct, 16 * tb + l16, kk, g);
+                // inter-chunk term y^T = H^T C^T with the state entering chunk c
+                f32x4 ye[4];
+                {
+                    X8 hf[KN];
+#pragma unroll
+                    for (int kk = 0; kk < KN; ++kk) {
+                        X4 lo, hi = {};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            lo[i] = cvt<T>(Hs[2 * kk][i]);
+                            if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[2 * kk + 1][i]);
+                        }
+                        hf[kk] = cat<X8, X4>(lo, hi);
                     }
-                    hf[kk] = cat<X8, X4>(lo, hi);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        ye[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < KN; ++kk) ye[tb] = mma(hf[kk], cf[tb][kk], ye[tb]);
+                    }
                 }
+                // C B^T tiles with t-block >= s-block, 3/3/2/2 per wave, masked
+                // with this quad's head decay
+                X8 a[KN];
+                auto bfrag = [&](int sb) {
+#pragma unroll
+                    for (int kk = 0; kk < KN; ++kk) a[kk] = tile_frag<N>(bt_tile, 16 * sb + l16, kk, g);
+                };
+                switch (w4) {
+                    case 0:
+                        bfrag(0);
+                        mask_tile<0, 0>(sm, D, q, lane, a, cf[0]);
+                        mask_tile<1, 0>(sm, D, q, lane, a, cf[1]);
+                        mask_tile<2, 0>(sm, D, q, lane, a, cf[2]);
+                        break;
+                    case 1:
+                        bfrag(1);
+                        mask_tile<1, 1>(sm, D, q, lane, a, cf[1]);
+                        mask_tile<2, 1>(sm, D, q, lane, a, cf[2]);
+                        mask_tile<3, 1>(sm, D, q, lane, a, cf[3]);
+                        break;
+                    case 2:
+                        bfrag(0);
+                        mask_tile<3, 0>(sm, D, q, lane, a, cf[3]);
+                        bfrag(2);
+                        mask_tile<2, 2>(sm, D, q, lane, a, cf[2]);
+                        break;
+                    default:
+                        bfrag(2);
+                        mask_tile<3, 2>(sm, D, q, lane, a, cf[3]);
+                        bfrag(3);
+                        mask_tile<3, 3>(sm, D, q, lane, a, cf[3]);
+                        break;
+                }
+                // chunk c+1's decay factors (its d_raw landed before this step)
+                if (w4 == DW && !last) decay_factors<T>(*decn, dnext[lane], p.d_init, clen_of(c + 1), lane);
+
+                block_sync();  // masked fragments and decay complete, C tile no longer read
+                if (!last) issue_c(c + 1, cn);
+
                 // X^T fragments in the K order of the mask tiles:
                 // tokens 32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3)
                 X8 xf[2];
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    xf[kk] = tok_frag<XU>(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, wc, lane);
+                    xf[kk] = tok_frag(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, w4, lane);
+                X8 lf[6];
+#pragma unroll
+                for (int s = 0; s < 6; ++s) lf[s] = sm.lf[q][s][lane];
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int th = 0; th < 2; ++th) {  // t-blocks 2*th, 2*th + 1
-                    // every operand of this half first, then the MFMAs
-                    X8 lfa[2], lfb[2], cf[2][KN];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        lfa[j] = sm.lf[q][lslot(2 * th + j, 0)][lane];
-                        if (th == 1) lfb[j] = sm.lf[q][lslot(2 + j, 1)][lane];
-                    }
-#pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) {
-                        const int n0 = 32 * kk + 4 * g, n1 = n0 + 16;
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int t = 16 * (2 * th + j) + l16;
-                            X4 c0 = {}, c1 = {};
-                            if (N % 32 == 0 || n0 < N) c0 = lds4<BU>(sm.cs, t, n0);
-                            if (N % 32 == 0 || n1 < N) c1 = lds4<BU>(sm.cs, t, n1);
-                            cf[j][kk] = cat<X8, X4>(c0, c1);
-                        }
-                    }
+                for (int tb = 0; tb < 4; ++tb) {
                     // intra-chunk: y^T += X^T L^T (causal fragments only)
-                    f32x4 yi[2], ye[2];
+                    f32x4 yi = mma(xf[0], lf[lslot(tb, 0)], z);
+                    if (tb >= 2) yi = mma(xf[1], lf[lslot(tb, 1)], yi);
+                    const int t = 16 * tb + l16;
+                    const float sc = D.fe[t];
+                    f32x4 o;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        yi[j] = mma(xf[0], lfa[j], z);
-                        if (th == 1) yi[j] = mma(xf[1], lfb[j], yi[j]);
-                    }
-                    // inter-chunk: y^T += H^T C^T, two independent chains
-                    ye[0] = z;
-                    ye[1] = z;
-#pragma unroll
-                    for (int kk = 0; kk < KN; ++kk)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) ye[j] = mma(hf[kk], cf[j][kk], ye[j]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int tb = 2 * th + j;
-                        const float sc = D.fe[16 * tb + l16];
-                        f32x4 o;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[i] = yi[j][i] + sc * ye[j][i];
-                        if (yo[tb] >= 0) store4(yh + yo[tb], o);
-                    }
+                    for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
+                    if (active && t < cl) store4_async(yh + (t0 + dir * t) * p.ys_t, o);
                 }
+            } else {
+                if (w4 == DW && !last) decay_factors<T>(*decn, dnext[lane], p.d_init, clen_of(c + 1), lane);
             }
-            if (need_update) {
+
+            if (!(SCAN && last)) {
                 // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
                 const float decay = D.fe[kChunk - 1];
 #pragma unroll
@@ -596,18 +672,21 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
                 for (int kk = 0; kk < kChunk / 32; ++kk) {
                     const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
                     const f32x8 ws = ld8(&D.w[s0]);
-                    const X8 xv = tok_frag<XU>(xt, s0, s0 + 4, wc, lane);
+                    const X8 xv = tok_frag(xt, s0, s0 + 4, w4, lane);
                     X8 b, bt[NB];
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) bt[nb] = tok_frag<BU>(sm.bs, s0, s0 + 4, 16 * nb, lane);
+                    for (int nb = 0; nb < NB; ++nb) bt[nb] = tok_frag(bt_tile, s0, s0 + 4, nb, lane);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) Hs[nb] = mma(bt[nb], b, Hs[nb]);
                 }
             }
-        }
-        if (!SCAN && w4 == 0 && q < nh) logdec2 += sm.dec[q].cs2[kChunk - 1];
+            if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
+        };
+        const int d1 = (c + 1) % 3, d2 = (c + 2) % 3;
+        body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.dr[d1][q], sm.xs[buf ^ 1][q], sm.bs[buf ^ 1],
+             sm.cs, sm.dr[d2][q], &sm.dec[buf ^ 1][q]);
     }
 
     if (!SCAN) {
@@ -616,7 +695,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) store4(sb + state_off(pb, nb, lane, NB), Hs[nb]);
         }
-        if (pg == 0 && w4 == 0 && q < nh && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
+        if (pg == 0 && w4 == 0 && live && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
     }
 }
 
