@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -118,6 +118,10 @@ typedef struct ssd_plan_info {
     int32_t col_groups;        /* headdim columns are split in groups of 64  */
     int64_t nspan;             /* span slots (upper bound with cu_seqlens)   */
     uint64_t workspace_bytes;  /* = ssd_fwd_workspace_bytes(dims)            */
+    int32_t fused_pass;        /* 1: SSD_STAGE_SCAN forms every span's incoming
+                                  state from the span states itself and
+                                  SSD_STAGE_PASS launches nothing (batch mode
+                                  with at most 16 spans per sequence)        */
 } ssd_plan_info;
 
 /* Fills *out for these sizes; returns the status ssd_fwd's size checks
@@ -128,7 +132,8 @@ int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out);
 enum {
     SSD_STAGE_TABLE = 1,  /* span table from cu_seqlens (no-op without them) */
     SSD_STAGE_STATE = 2,  /* per-span local states and decays               */
-    SSD_STAGE_PASS = 4,   /* state passing across spans, final_state        */
+    SSD_STAGE_PASS = 4,   /* state passing across spans, final_state (folded
+                             into SSD_STAGE_SCAN when the plan says so)     */
     SSD_STAGE_SCAN = 8,   /* per-chunk outputs y                            */
     SSD_STAGE_ALL = 15
 };

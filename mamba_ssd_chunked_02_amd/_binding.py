@@ -47,6 +47,7 @@ class SsdPlanInfo(ctypes.Structure):
         ("col_groups", ctypes.c_int32),
         ("nspan", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
+        ("fused_pass", ctypes.c_int32),
     ]
 
 

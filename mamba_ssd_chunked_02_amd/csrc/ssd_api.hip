@@ -25,6 +25,7 @@ struct Plan {
     int32_t npg = 0;        // headdim column groups
     int32_t hg_state = 1;   // heads per span_state workgroup
     int32_t hg_scan = 1;    // heads per span_scan workgroup
+    int32_t fuse = 0;       // span_scan forms incoming states (no state_pass launch)
     int64_t nspan = 0;      // span slots
     size_t off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
     size_t total = 0;
@@ -88,6 +89,15 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     } else {
         pl->sps = (int32_t)ceil_div(ceil_div(d->seqlen, kChunk), pl->K);
         pl->nspan = (int64_t)d->batch * pl->sps;
+        // Few spans per sequence: span_scan folds the earlier span states of
+        // its sequence itself, which saves the state_pass launch.  Empty
+        // sequences keep the pass, which copies init_state to final_state.
+        // SSD_FUSE_PASS=0 / 1 forces either path (tests, sweeps).
+        pl->fuse = pl->sps > 0 && pl->sps <= ssd::kFuseSpans;
+        if (const char* e = getenv("SSD_FUSE_PASS")) {
+            if (e[0] == '0') pl->fuse = 0;
+            if (e[0] == '1') pl->fuse = 1;
+        }
     }
     size_t off = 0;
     pl->off_states = off;
@@ -161,6 +171,7 @@ int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out) {
     out->col_groups = pl.npg;
     out->nspan = pl.nspan;
     out->workspace_bytes = pl.total;
+    out->fused_pass = pl.fuse;
     return SSD_OK;
 }
 
@@ -235,6 +246,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.hg_state = pl.hg_state;
     p.hg_scan = pl.hg_scan;
     p.reverse = reverse;
+    p.fuse_pass = pl.fuse;
     p.d_init = d_init;
 
     hipError_t e = hipSuccess;
@@ -253,7 +265,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
         e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
-    if (mask & SSD_STAGE_PASS) {
+    if ((mask & SSD_STAGE_PASS) && !pl.fuse) {
         e = ssd::launch_state_pass(p, d.dtype, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }

@@ -40,8 +40,15 @@ struct KParams {
     int32_t hg_state;       // heads per span_state workgroup (divides H/G)
     int32_t hg_scan;        // heads per span_scan workgroup (divides H/G)
     int32_t reverse;
+    int32_t fuse_pass;      // batch mode, few spans per sequence: span_scan forms
+                            // each span's incoming state from the span states
+                            // itself and writes final_state (no state_pass)
     float d_init;
 };
+
+// Most spans per sequence for which span_scan forms the incoming states
+// itself (each workgroup folds all earlier spans of its sequence).
+constexpr int kFuseSpans = 16;
 
 // Launchers (ssd_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,

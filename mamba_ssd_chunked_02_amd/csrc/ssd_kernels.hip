@@ -324,10 +324,11 @@ __device__ __forceinline__ int64_t state_off(int pb, int nb, int lane, int NB) {
     return ((int64_t)(pb * NB + nb) * 64 + lane) * 4;
 }
 
-// LDS of one span workgroup.  X and B tiles and the decay factors are
-// double-buffered: chunk c+1's fill one buffer while chunk c is computed
-// from the other; d_raw arrives two chunks ahead (three buffers).  The C
-// tile has one buffer, refilled as soon as the step's C reads are done.
+// LDS of one span workgroup.  X and B tiles are double-buffered: chunk
+// c+1's fill one buffer while chunk c is computed from the other.  The C tile
+// has one buffer, refilled as soon as the step's C reads are done.  Decay
+// factors are formed four chunks at a time (one chunk per wave of a quad)
+// from d_raw loaded one such batch ahead.
 template <typename T, int N, int HG, bool SCAN>
 struct __attribute__((aligned(16))) Smem {
     using X8 = typename Vec<T>::x8;
@@ -335,12 +336,12 @@ struct __attribute__((aligned(16))) Smem {
     T bs[2][kChunk * N];                // B
     T cs[SCAN ? kChunk * N : 1];        // C (scan)
     X8 lf[SCAN ? HG : 1][SCAN ? 6 : 1][SCAN ? 64 : 1];  // masked C B^T per head (scan)
-    Decay dec[2][HG];                   // per head
-    uint32_t dr[3][HG][kChunk];         // d_raw per head, one token per lane
+    Decay dec[kWaves][HG];              // chunk 4b + w of the current batch b, per head
+    uint32_t dr[2][kWaves][HG][kChunk]; // d_raw of a batch, one token per lane
 };
 
-// One wave forms a head's decay factors from d_raw as loaded into LDS (a
-// bf16 value sits in the low half of its 32-bit slot).
+// One wave forms a head's decay factors for one chunk from d_raw as loaded
+// into LDS (a bf16 value sits in the low half of its 32-bit slot).
 template <typename T>
 __device__ __forceinline__ void decay_factors(Decay& D, uint32_t raw, float d_init, int clen,
                                               int lane) {
@@ -418,7 +419,6 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     constexpr int NB = Cf::NB, KN = Cf::KN, EPU = Cf::EPU;
     constexpr int W = 16 / EPU;               // 16-byte units per block row
     constexpr int XI = 4 * W, BI = NB * W;    // load instructions per X / B / C tile
-    constexpr int DW = 3;                     // wave of each quad that forms the decay
     __shared__ Smem<T, N, HG, SCAN> sm;
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
             issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cg + tok0(c) * GN, dir * GN, wave,
                                                             clen_of(c), N, lane);
     };
-    // The quad head's d_raw of chunk c, one token per lane (decay wave only).
+    // The quad head's d_raw of chunk c, one token per lane.
     auto issue_d = [&](int c, uint32_t* __restrict__ ddst) {
         const int cl = clen_of(c);
         const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * p.H);
@@ -506,13 +506,42 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
         else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
     };
 
+    // The state entering the span, this wave's 16 columns, MFMA result order.
+    // Span scan, separate state pass: read it (the pass replaced each span
+    // state by it).  Span scan, pass folded in (batch mode): fold the span
+    // states of the earlier spans of this sequence in order, from the initial
+    // state, H <- a_j H + S_j in fp32.  The last span of a sequence then also
+    // advances over its last chunk and writes final_state.
     f32x4 Hs[NB];
-    {
+    const int kin = (int)(span % (p.sps > 0 ? p.sps : 1));  // span within its sequence
+    const bool write_final = SCAN && p.fuse_pass && p.final_state && kin == p.sps - 1;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (n, p) of this lane's entry i of state block nb, [N][P] offset
+    auto np_off = [&](int nb, int i) -> int64_t {
+        return (int64_t)(16 * nb + 4 * g + i) * p.P + 16 * pb + l16;
+    };
+    const int64_t hseq = ((span - kin) / (p.sps > 0 ? p.sps : 1) * p.H + h) * (int64_t)N * p.P;
+    if (SCAN && active && !p.fuse_pass) {
         const T* sb = (const T*)p.states + (span * p.H + h) * (int64_t)p.P * N;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (SCAN && active) Hs[nb] = load4(sb + state_off(pb, nb, lane, NB));
+        for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(sb + state_off(pb, nb, lane, NB));
+    }
+    if (SCAN && active && p.fuse_pass) {
+        if (p.init) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Hs[nb][i] = p.init[hseq + np_off(nb, i)];
+        }
+        // (all workgroups fold at once, so this is bound by the bytes read,
+        // not by the latency of the sequential loop)
+        const int64_t sp0 = span - kin;
+        for (int j = 0; j < kin; ++j) {
+            const float a = p.decay[(sp0 + j) * p.H + h];
+            const T* sj = (const T*)p.states + ((sp0 + j) * p.H + h) * (int64_t)p.P * N;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Hs[nb] = a * Hs[nb] + load4(sj + state_off(pb, nb, lane, NB));
         }
     }
     float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
@@ -530,45 +559,47 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     T* const yh = (T*)p.y + pcol0 + w4 * 16 + 4 * g + (int64_t)h * p.ys_h;
 
     // Software pipeline over the span's chunks; step c:
-    //   wait for chunk c's tiles; barrier; issue chunk c+1's X and B tiles
-    //   and chunk c+2's d_raw into the free buffers; (scan) the inter-chunk
-    //   term H^T C^T and the masked C B^T; the decay wave forms chunk c+1's
-    //   decay factors; (scan) barrier, issue chunk c+1's C tile, write y;
-    //   advance the state.
+    //   wait for chunk c's tiles; barrier; (every fourth step) each wave
+    //   forms one of the next four chunks' decay factors, barrier, and loads
+    //   d_raw of the four after; issue chunk c+1's X and B tiles into the
+    //   free buffers; (scan) the inter-chunk term H^T C^T and the masked
+    //   C B^T, barrier, issue chunk c+1's C tile, write y; advance the state.
     // Only loads into LDS are in flight across a step, and the explicit wait
     // at its top covers them; the compiler itself never waits for them (the
     // restrict qualifiers below tell it that the step's LDS reads and the
     // loads it issues touch different buffers).
-    if (w4 == DW) {
-        issue_d(0, sm.dr[0][q]);
-        if (nck > 1) issue_d(1, sm.dr[1][q]);
-    }
+    if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
+    if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
     issue_xb(0, sm.xs[0][q], sm.bs[0]);
     issue_c(0, sm.cs);
     vm_wait<0>();
-    if (w4 == DW) decay_factors<T>(sm.dec[0][q], sm.dr[0][q][lane], p.d_init, clen_of(0), lane);
+    if (w4 < nck) decay_factors<T>(sm.dec[w4][q], sm.dr[0][w4][q][lane], p.d_init, clen_of(w4), lane);
 
     for (int c = 0; c < nck; ++c) {
         const bool last = c + 1 == nck;
         const int buf = c & 1;
         const int cl = clen_of(c);
         const int64_t t0 = tok0(c);
-        const Decay& D = sm.dec[buf][q];
+        const Decay& D = sm.dec[c % kWaves][q];
 
         // After chunk c's loads this wave issued, in an active scan wave,
         // exactly four y stores (the previous chunk is full), else nothing.
         if (SCAN && active && c > 0) vm_wait<4>();
         else vm_wait<0>();
-        block_sync();  // every wave's loads of chunk c and its decay factors are in LDS
+        block_sync();  // every wave's loads of chunk c are in LDS
+        if (c > 0 && c % kWaves == 0) {
+            // batch c/4: its d_raw was loaded four steps ago
+            const int bb = (c / kWaves) & 1;
+            if (c + w4 < nck)
+                decay_factors<T>(sm.dec[w4][q], sm.dr[bb][w4][q][lane], p.d_init, clen_of(c + w4), lane);
+            block_sync();
+            if (c + kWaves + w4 < nck) issue_d(c + kWaves + w4, sm.dr[bb ^ 1][w4][q]);
+        }
 
         auto body = [&](const T* __restrict__ xt, const T* __restrict__ bt_tile,
-                        const T* __restrict__ ct, const uint32_t* __restrict__ dnext,
-                        T* __restrict__ xn, T* __restrict__ bn, T* __restrict__ cn,
-                        uint32_t* __restrict__ dn2, Decay* __restrict__ decn) {
-            if (!last) {
-                issue_xb(c + 1, xn, bn);
-                if (w4 == DW && c + 2 < nck) issue_d(c + 2, dn2);
-            }
+                        const T* __restrict__ ct, T* __restrict__ xn, T* __restrict__ bn,
+                        T* __restrict__ cn) {
+            if (!last) issue_xb(c + 1, xn, bn);
 
             if constexpr (SCAN) {
                 // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
@@ -631,10 +662,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
                         mask_tile<3, 3>(sm, D, q, lane, a, cf[3]);
                         break;
                 }
-                // chunk c+1's decay factors (its d_raw landed before this step)
-                if (w4 == DW && !last) decay_factors<T>(*decn, dnext[lane], p.d_init, clen_of(c + 1), lane);
-
-                block_sync();  // masked fragments and decay complete, C tile no longer read
+                block_sync();  // masked fragments complete, C tile no longer read
                 if (!last) issue_c(c + 1, cn);
 
                 // X^T fragments in the K order of the mask tiles:
@@ -659,11 +687,9 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
                     for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
                     if (active && t < cl) store4_async(yh + (t0 + dir * t) * p.ys_t, o);
                 }
-            } else {
-                if (w4 == DW && !last) decay_factors<T>(*decn, dnext[lane], p.d_init, clen_of(c + 1), lane);
             }
 
-            if (!(SCAN && last)) {
+            if (!(SCAN && last) || write_final) {
                 // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
                 const float decay = D.fe[kChunk - 1];
 #pragma unroll
@@ -684,11 +710,15 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
             }
             if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
         };
-        const int d1 = (c + 1) % 3, d2 = (c + 2) % 3;
-        body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.dr[d1][q], sm.xs[buf ^ 1][q], sm.bs[buf ^ 1],
-             sm.cs, sm.dr[d2][q], &sm.dec[buf ^ 1][q]);
+        body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.xs[buf ^ 1][q], sm.bs[buf ^ 1], sm.cs);
     }
 
+    if (write_final && active) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.final_state[hseq + np_off(nb, i)] = Hs[nb][i];
+    }
     if (!SCAN) {
         if (active) {
             T* sb = (T*)p.states + (span * p.H + h) * (int64_t)p.P * N;

@@ -119,3 +119,18 @@ def test_binding_rejects_cpu_mismatch(m):
     with pytest.raises(ValueError):
         m.ssd_fwd(x, torch.zeros(1, 64, 3), -4.6, torch.zeros(1, 64, 1, 16),
                   torch.zeros(1, 64, 1, 16))
+
+
+def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
+    """Batch mode with at most 16 spans per sequence folds the state pass
+    into span_scan; packed sequences and longer ones keep the pass kernel."""
+    monkeypatch.delenv("SSD_FUSE_PASS", raising=False)
+    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
+    layer = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128))
+    assert layer.chunks_per_span == 4 and layer.fused_pass == 1
+    long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 17, 2, 64, 128))
+    assert long.fused_pass == 0
+    varlen = m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3))
+    assert varlen.fused_pass == 0
+    monkeypatch.setenv("SSD_FUSE_PASS", "0")
+    assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).fused_pass == 0

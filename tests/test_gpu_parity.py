@@ -169,6 +169,23 @@ def test_span_length_invariance(ssd, k, monkeypatch):
     check(ssd, q, True, label=f"K={k} varlen rev f32")
 
 
+@pytest.mark.parametrize("fuse", ["0", "1"])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
+    """Both ways of handing the state from span to span match the oracle: the
+    separate state_pass kernel, and span_scan folding the earlier span states
+    of its sequence itself (which also writes final_state)."""
+    monkeypatch.setenv("SSD_FUSE_PASS", fuse)
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+    p = random_problem(151, 2, 1000, 3, 64, 128, dtype="bf16", init_scale=0.5)
+    d = to_dev(p)
+    call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+    assert ssd.ssd_fwd_plan(call.dims).fused_pass == int(fuse)
+    check(ssd, p, reverse, label=f"fuse={fuse} bf16")
+    q = random_problem(157, 3, 500, 2, 32, 64, dtype="f32", init_scale=0.5)
+    check(ssd, q, reverse, label=f"fuse={fuse} f32")
+
+
 def test_empty_sequence_keeps_init(ssd):
     p = random_problem(137, 2, 0, 2, 16, 16, dtype="bf16", init_scale=1.0)
     y, f = run(ssd, p)
