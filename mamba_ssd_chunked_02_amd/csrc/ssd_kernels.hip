@@ -300,7 +300,7 @@ __device__ __forceinline__ typename Vec<T>::x8 tile_frag(const T* tile, int r, i
 //   e^{cs_t - cs_s} d_s = fa_s * fm(tb, sb) * fb_t,
 //   fa_s = 2^{c_{sb+1} - cs_s} d_s,  fm = 2^{c_tb - c_{sb+1}},  fb_t = 2^{cs_t - c_tb},
 // each factor <= 1, so off-diagonal mask tiles need no exponentials.
-struct Decay {
+struct __attribute__((aligned(16))) Decay {  // read with 16-byte vector loads
     float cs2[kChunk];  // cs
     float dt[kChunk];   // d_s (0 past the end of the sequence)
     float w[kChunk];    // 2^{cs_last - cs_s} d_s   (state update weights)
@@ -331,13 +331,16 @@ __device__ __forceinline__ int64_t state_off(int pb, int nb, int lane, int NB) {
 // from d_raw loaded one such batch ahead.
 template <typename T, int N, int HG, bool SCAN>
 struct __attribute__((aligned(16))) Smem {
-    using X8 = typename Vec<T>::x8;
+    using X4 = typename Vec<T>::x4;
     T xs[2][HG][kChunk * kPGroup];      // X of every head, this group's 64 columns
     T bs[2][kChunk * N];                // B
     T cs[SCAN ? kChunk * N : 1];        // C (scan)
-    X8 lf[SCAN ? HG : 1][SCAN ? 6 : 1][SCAN ? 64 : 1];  // masked C B^T per head (scan)
+    // masked C B^T per head (scan): fragment slot, half, lane -- each half a
+    // contiguous run of 64 8-byte (bf16) values, so writes and reads of one
+    // half never share a bank
+    X4 lf[SCAN ? HG : 1][SCAN ? 6 : 1][2][SCAN ? 64 : 1];
     Decay dec[kWaves][HG];              // chunk 4b + w of the current batch b, per head
-    uint32_t dr[2][kWaves][HG][kChunk]; // d_raw of a batch, one token per lane
+    __attribute__((aligned(16))) uint32_t dr[2][kWaves][HG][kChunk];  // d_raw of a batch, per lane
 };
 
 // One wave forms a head's decay factors for one chunk from d_raw as loaded
@@ -399,7 +402,7 @@ __device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay&
             v[i] = cvt<T>(causal ? acc[i] * e * dts[i] : 0.f);
         }
     }
-    if constexpr (SCAN) *((X4*)&sm.lf[q][lslot(TB, SB >> 1)][lane] + (SB & 1)) = v;
+    if constexpr (SCAN) sm.lf[q][lslot(TB, SB >> 1)][SB & 1][lane] = v;
 }
 
 // Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
@@ -477,24 +480,31 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     const T* const bg = (const T*)p.B + (int64_t)grp * N;
     const T* const cg = (const T*)p.C + (int64_t)grp * N;
     const T* const dg = (const T*)p.d_raw + hc;
-    auto tok0 = [&](int c) -> int64_t {
-        const int64_t j0 = (int64_t)(chunk0 + c) * kChunk;
-        return start + (p.reverse ? len - 1 - j0 : j0);
-    };
-    auto clen_of = [&](int c) -> int { return (int)imin(kChunk, len - (int64_t)(chunk0 + c) * kChunk); };
+    // Row 0 of chunk c is token tb0 + c * dstep; its tokens left in the
+    // sequence are rem0 - 64c.
+    const int64_t cj0 = (int64_t)chunk0 * kChunk;
+    const int64_t tb0 = start + (p.reverse ? len - 1 - cj0 : cj0);
+    const int dstep = dir * kChunk;
+    const int64_t rem0 = len - cj0;
+    auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(c * dstep); };
+    auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
+    // chunk c's row-0 pointers: base at chunk 0 plus c chunk steps
+    const T* const xc0 = xg + tb0 * HP;
+    const T* const bc0 = bg + tb0 * GN;
+    const T* const cc0 = cg + tb0 * GN;
+    const int64_t xcs = (int64_t)dstep * HP, bcs = (int64_t)dstep * GN;
     // Chunk c's X tile (wave w4 loads its own 16-column block) and this
     // wave's share of the B tile.
     auto issue_xb = [&](int c, T* __restrict__ xdst, T* __restrict__ bdst) {
-        const int64_t t0 = tok0(c);
         const int cl = clen_of(c);
-        issue_tile<W, 1, XI>(xdst, xg + t0 * HP, dir * HP, w4 * W, cl, pgw, lane);
-        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bg + t0 * GN, dir * GN, wave, cl, N,
+        issue_tile<W, 1, XI>(xdst, xc0 + c * xcs, dir * HP, w4 * W, cl, pgw, lane);
+        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + c * bcs, dir * GN, wave, cl, N,
                                                         lane);
     };
     // This wave's share of chunk c's C tile (scan).
     auto issue_c = [&](int c, T* __restrict__ cdst) {
         if constexpr (SCAN)
-            issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cg + tok0(c) * GN, dir * GN, wave,
+            issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cc0 + c * bcs, dir * GN, wave,
                                                             clen_of(c), N, lane);
     };
     // The quad head's d_raw of chunk c, one token per lane.
@@ -551,12 +561,16 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
         // (tb, sb) = (0, 1) and (2, 3)
         for (int i = tid; i < HG * 2 * 64; i += Cf::TH) {
             const int hh = i / 128, k = (i / 64) & 1, l = i & 63;
-            X4* dst = (X4*)&sm.lf[hh][k ? lslot(2, 1) : lslot(0, 0)][l] + 1;
-            *dst = X4{};
+            sm.lf[hh][k ? lslot(2, 1) : lslot(0, 0)][1][l] = X4{};
         }
     }
 
-    T* const yh = (T*)p.y + pcol0 + w4 * 16 + 4 * g + (int64_t)h * p.ys_h;
+    // y row of token t of chunk c: yc0 + c * ycs + yoff[t / 16] for this lane's t
+    T* const yc0 = (T*)p.y + pcol0 + w4 * 16 + 4 * g + (int64_t)h * p.ys_h + tb0 * p.ys_t;
+    const int64_t ycs = (int64_t)dstep * p.ys_t;
+    int64_t yoff[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) yoff[tb] = (int64_t)(dir * (16 * tb + l16)) * p.ys_t;
 
     // Software pipeline over the span's chunks; step c:
     //   wait for chunk c's tiles; barrier; (every fourth step) each wave
@@ -579,7 +593,6 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
         const bool last = c + 1 == nck;
         const int buf = c & 1;
         const int cl = clen_of(c);
-        const int64_t t0 = tok0(c);
         const Decay& D = sm.dec[c % kWaves][q];
 
         // After chunk c's loads this wave issued, in an active scan wave,
@@ -673,7 +686,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
                     xf[kk] = tok_frag(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, w4, lane);
                 X8 lf[6];
 #pragma unroll
-                for (int s = 0; s < 6; ++s) lf[s] = sm.lf[q][s][lane];
+                for (int s = 0; s < 6; ++s) lf[s] = cat<X8, X4>(sm.lf[q][s][0][lane], sm.lf[q][s][1][lane]);
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
                     f32x4 o;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
-                    if (active && t < cl) store4_async(yh + (t0 + dir * t) * p.ys_t, o);
+                    if (active && t < cl) store4_async(yc0 + c * ycs + yoff[tb], o);
                 }
             }
 
