@@ -37,8 +37,9 @@ METRIC = "SSD chunked-scan fwd Mtokens/s at 1 GPU; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc", "ssd_kernels.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_layer.json")
-STAGE_KERNEL = {"state": "span_kernel<bf16, N, false>", "pass": "state_pass_kernel",
-                "scan": "span_kernel<bf16, N, true>", "table": "span_table_kernel"}
+STAGE_KERNEL = {"state": "span_kernel<bf16, N, 1, kModeState>", "pass": "state_pass_kernel",
+                "scan": "span_kernel<bf16, N, 1, kModeScan>",
+                "fused": "span_kernel<bf16, N, 1, kModeFused>", "table": "span_table_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -53,9 +54,12 @@ def stage_bytes(w, plan, spans_used: int) -> dict:
     Per token-head unit (T*H units): x (P*e), d_raw (e), B and C (N*e each,
     shared by the H/G heads of a group), y (P*e).  Per span-head: one N x P
     state stored in the input type (plus a 4-byte fp32 decay); init and
-    final states are fp32.  e = element size of the inputs.  When the plan
-    folds the state pass into span_scan, span_scan is charged each span
-    state and decay once, plus init and final states, and there is no pass."""
+    final states are fp32.  e = element size of the inputs.
+    fused_pass 1: span_scan is charged each span state and decay once, plus
+    init and final states, and there is no pass.  fused_pass 2: the one
+    launch is charged its inputs and outputs plus each span state it hands
+    on (all but the last span of a sequence) written once; the reads of
+    those states by later spans are not counted."""
     e = 2 if w.dtype == "bf16" else 4
     T, H, P, N, G = w.tokens, w.nheads, w.headdim, w.d_state, w.ngroups
     S = w.nstates
@@ -67,7 +71,10 @@ def stage_bytes(w, plan, spans_used: int) -> dict:
     dec = spans_used * H * 4
     fin = S * H * N * P * 4
     init = fin if w.init != "zeros" else 0
-    if plan.fused_pass:
+    if plan.fused_pass == 2:
+        handed = (spans_used - S) * H
+        return {"fused": x + draw + 2 * bc + y + init + fin + handed * (N * P * e + 4)}
+    if plan.fused_pass == 1:
         return {"state": x + draw + bc + st + dec,
                 "scan": x + draw + 2 * bc + st + dec + init + fin + y}
     return {
@@ -188,8 +195,10 @@ def main() -> int:
 
     # per-kernel durations: HIP events around every stage on the launch stream
     stages = [("state", m.STAGE_STATE), ("pass", m.STAGE_PASS), ("scan", m.STAGE_SCAN)]
-    if plan.fused_pass:
+    if plan.fused_pass == 1:
         stages = [st for st in stages if st[0] != "pass"]
+    if plan.fused_pass == 2:
+        stages = [("fused", m.STAGE_SCAN)]
     if w.nseq:
         stages = [("table", m.STAGE_TABLE)] + stages
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -96,7 +96,15 @@ size_t ssd_fwd_workspace_bytes(const ssd_dims* dims);
  *               strides in elements, multiples of 16 bytes
  *   final_state output [S, H, N, P] float32, or NULL to skip
  *   workspace   device scratch of at least ssd_fwd_workspace_bytes(dims)
- *               bytes, 256-byte aligned; contents need no initialisation
+ *               bytes, 256-byte aligned.  Zero-fill it once before its
+ *               first use; after that leave it alone between calls (each
+ *               call leaves it ready for the next, whatever its sizes).
+ *               Its first 256 bytes are a header of 32-bit words: word 0
+ *               counts the fused launches, word 1 is their ticket counter
+ *               (0 between calls), word 2 counts flag waits that ran out
+ *               (stays 0 unless the header was not zero-filled; the results
+ *               of such a call are unspecified).  Calls that overlap in time
+ *               need separate workspaces.
  *   stream      hipStream_t to launch on (NULL = default stream)
  * S is b without cu_seqlens and nseq with them.  x, B, C and y must be
  * 16-byte aligned; they may be NULL only when b*L == 0.  Returns SSD_OK once
@@ -118,10 +126,16 @@ typedef struct ssd_plan_info {
     int32_t col_groups;        /* headdim columns are split in groups of 64  */
     int64_t nspan;             /* span slots (upper bound with cu_seqlens)   */
     uint64_t workspace_bytes;  /* = ssd_fwd_workspace_bytes(dims)            */
-    int32_t fused_pass;        /* 1: SSD_STAGE_SCAN forms every span's incoming
-                                  state from the span states itself and
-                                  SSD_STAGE_PASS launches nothing (batch mode
-                                  with at most 16 spans per sequence)        */
+    int32_t fused_pass;        /* 0: stages STATE, PASS and SCAN launch one
+                                  kernel each.  1: SCAN forms every span's
+                                  incoming state from the span states itself
+                                  and PASS launches nothing.  2: SCAN is one
+                                  launch that does STATE, PASS and SCAN
+                                  (their workgroups hand span states to each
+                                  other); STATE and PASS launch nothing.
+                                  1 is the default in batch mode with 1..16
+                                  spans per sequence, else 0; the environment
+                                  variable SSD_FUSE_PASS=0/1/2 forces one.  */
 } ssd_plan_info;
 
 /* Fills *out for these sizes; returns the status ssd_fwd's size checks
@@ -131,9 +145,10 @@ int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out);
 /* Stages of ssd_fwd, one kernel launch each, in this order. */
 enum {
     SSD_STAGE_TABLE = 1,  /* span table from cu_seqlens (no-op without them) */
-    SSD_STAGE_STATE = 2,  /* per-span local states and decays               */
+    SSD_STAGE_STATE = 2,  /* per-span local states and decays (folded into
+                             SSD_STAGE_SCAN when fused_pass is 2)           */
     SSD_STAGE_PASS = 4,   /* state passing across spans, final_state (folded
-                             into SSD_STAGE_SCAN when the plan says so)     */
+                             into SSD_STAGE_SCAN when fused_pass is 1 or 2) */
     SSD_STAGE_SCAN = 8,   /* per-chunk outputs y                            */
     SSD_STAGE_ALL = 15
 };

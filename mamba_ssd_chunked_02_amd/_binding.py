@@ -2,7 +2,8 @@
 
 Every step of the scan runs in the HIP library; this module maps torch
 tensors to pointers and sizes, allocates outputs and workspace with torch,
-and passes torch's current HIP stream.  If libssd.so is missing the import
+and passes torch's current HIP stream.  Workspaces it allocates start
+zero-filled, as the library requires before a workspace's first use.  If libssd.so is missing the import
 of the library raises -- there is no fallback path.
 """
 from __future__ import annotations
@@ -222,7 +223,7 @@ def prepare(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlen
     dims = dims_for(x, B, chunk_size, cu_seqlens)
     need = ssd_fwd_workspace_bytes(dims)  # 0 for invalid sizes: ssd_fwd reports why
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     args = (_ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
             _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0,
             _ptr(y), y.stride(1), y.stride(2), _ptr(final_state),
@@ -242,7 +243,7 @@ def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,
     y = torch.empty((b, L, H, 2 * P), dtype=x.dtype, device=x.device)
     if workspace is None:
         need = ssd_fwd_workspace_bytes(dims_for(x, B, chunk_size, cu_seqlens))
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=x.device)
     _, ff = ssd_fwd(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, False,
                     y=y[..., :P], final_state=final_state, workspace=workspace)
     _, fr = ssd_fwd(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, True,

@@ -25,9 +25,10 @@ struct Plan {
     int32_t npg = 0;        // headdim column groups
     int32_t hg_state = 1;   // heads per span_state workgroup
     int32_t hg_scan = 1;    // heads per span_scan workgroup
-    int32_t fuse = 0;       // span_scan forms incoming states (no state_pass launch)
+    int32_t fuse = 0;       // 1: span_scan forms incoming states (no state_pass
+                            // launch); 2: one fused launch does every stage
     int64_t nspan = 0;      // span slots
-    size_t off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
+    size_t off_sync = 0, off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
     size_t total = 0;
 };
 
@@ -91,15 +92,30 @@ int make_plan(const ssd_dims* d, Plan* pl) {
         pl->nspan = (int64_t)d->batch * pl->sps;
         // Few spans per sequence: span_scan folds the earlier span states of
         // its sequence itself, which saves the state_pass launch.  Empty
-        // sequences keep the pass, which copies init_state to final_state.
-        // SSD_FUSE_PASS=0 / 1 forces either path (tests, sweeps).
-        pl->fuse = pl->sps > 0 && pl->sps <= ssd::kFuseSpans;
+        // sequences keep the three launches (state_pass copies init_state to
+        // final_state).  SSD_FUSE_PASS=0 / 1 / 2 forces the three launches,
+        // these two, or one fused launch whose workgroups hand the span
+        // states to the later spans of their sequence (as fast as the two
+        // launches at the sizes measured, so not the default).
+        const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
+        pl->fuse = pl->sps > 0 && pl->sps <= ssd::kFuseSpans ? 1 : 0;
         if (const char* e = getenv("SSD_FUSE_PASS")) {
-            if (e[0] == '0') pl->fuse = 0;
-            if (e[0] == '1') pl->fuse = 1;
+            if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) pl->fuse = e[0] - '0';
         }
+        if (pl->sps == 0) pl->fuse = 0;
+        if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) pl->fuse = 1;
     }
+    // The header sits at the start of every plan's workspace; the fused
+    // launch's words follow it: one 64-bit ticket/epoch word per chain
+    // (sequence, head group, column group), then one flag per workgroup.
     size_t off = 0;
+    pl->off_sync = off;
+    off = align_up(off + ssd::kSyncHeader * sizeof(uint32_t));
+    if (pl->fuse == 2) {
+        const int64_t chains = (int64_t)d->batch * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
+        off = align_up(off + (size_t)chains * sizeof(uint64_t) +
+                       (size_t)pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg * sizeof(uint32_t));
+    }
     pl->off_states = off;
     const size_t esz = d->dtype == SSD_BF16 ? 2 : 4;  // span states use the input type
     off = align_up(off + (size_t)pl->nspan * d->nheads * d->headdim * d->d_state * esz);
@@ -247,6 +263,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.hg_scan = pl.hg_scan;
     p.reverse = reverse;
     p.fuse_pass = pl.fuse;
+    p.sync = (uint32_t*)(ws + pl.off_sync);
     p.d_init = d_init;
 
     hipError_t e = hipSuccess;
@@ -261,7 +278,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
             if (e != hipSuccess) return SSD_ERR_HIP;
         }
     }
-    if (mask & SSD_STAGE_STATE) {
+    if ((mask & SSD_STAGE_STATE) && pl.fuse != 2) {
         e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }

@@ -40,15 +40,29 @@ struct KParams {
     int32_t hg_state;       // heads per span_state workgroup (divides H/G)
     int32_t hg_scan;        // heads per span_scan workgroup (divides H/G)
     int32_t reverse;
-    int32_t fuse_pass;      // batch mode, few spans per sequence: span_scan forms
-                            // each span's incoming state from the span states
-                            // itself and writes final_state (no state_pass)
+    int32_t fuse_pass;      // batch mode, few spans per sequence.  1: span_scan
+                            // forms each span's incoming state from the span
+                            // states itself and writes final_state (no
+                            // state_pass).  2: one fused launch does all.
+    uint32_t* sync;         // workspace header; for fuse_pass 2 followed by one
+                            // 64-bit ticket/epoch word per chain and one flag
+                            // per workgroup
     float d_init;
 };
 
 // Most spans per sequence for which span_scan forms the incoming states
 // itself (each workgroup folds all earlier spans of its sequence).
 constexpr int kFuseSpans = 16;
+
+// The workspace header: its first 256 bytes, of which word 2 counts the
+// fused launch's bounded flag waits that ran out.  The fused launch keeps
+// its ticket/epoch words and flags after it; all are zero before the first
+// call and left ready for the next call of the same sizes by every call.
+constexpr int kSyncTimeouts = 2;
+constexpr int kSyncHeader = 64;
+// Polls (each followed by a 64-cycle sleep) one workgroup spends at most
+// waiting for the flags of the earlier spans of its sequence.
+constexpr uint32_t kSpinBudget = 1u << 20;
 
 // Launchers (ssd_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,

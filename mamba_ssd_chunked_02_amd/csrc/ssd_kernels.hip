@@ -46,6 +46,7 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -91,6 +92,7 @@ template <typename T>
 __device__ __forceinline__ T cvt(float v) { return (T)v; }
 
 __device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+constexpr int imin_c(int a, int b) { return a < b ? a : b; }
 
 // Four consecutive outputs of one token: 8-byte (bf16) or 16-byte (fp32) store.
 __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
@@ -341,6 +343,7 @@ struct __attribute__((aligned(16))) Smem {
     X4 lf[SCAN ? HG : 1][SCAN ? 6 : 1][2][SCAN ? 64 : 1];
     Decay dec[kWaves][HG];              // chunk 4b + w of the current batch b, per head
     __attribute__((aligned(16))) uint32_t dr[2][kWaves][HG][kChunk];  // d_raw of a batch, per lane
+    uint32_t ticket, epoch;  // fused kernel: this workgroup's ticket and epoch
 };
 
 // One wave forms a head's decay factors for one chunk from d_raw as loaded
@@ -408,13 +411,75 @@ __device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay&
 // Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
 // per CU, or one 8-wave one; lighter variants get more from their natural
 // register use.  A scan with state rows wider than 256 bytes gets 512.
-template <typename T, int N, int HG, bool SCAN>
+enum { kModeState = 0, kModeScan = 1, kModeFused = 2 };
+template <typename T, int N, int HG, int MODE>
 constexpr int span_occupancy() {
-    return HG == 1 && !(SCAN && N * sizeof(T) > 256) ? 2 : 1;
+    return HG == 1 && !(MODE != kModeState && N * sizeof(T) > 256) ? 2 : 1;
 }
 
-template <typename T, int N, int HG, bool SCAN>
-__global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) void span_kernel(
+// Accesses coherent across the whole device (agent scope, all XCDs): the
+// span states, decays and flags that workgroups of one launch hand to each
+// other.  Stores write through to the point of coherence; loads read from it.
+__device__ __forceinline__ void coherent_store32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t coherent_load32(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store64(void* p, uint64_t v) {
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t coherent_load64(const void* p) {
+    return __hip_atomic_load((uint64_t*)const_cast<void*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+// Four state entries, stored in the input type (8 or 16 bytes).
+__device__ __forceinline__ void coherent_store4(bf16* p, const f32x4& v) {
+    bf16x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (bf16)v[i];
+    coherent_store64(p, __builtin_bit_cast(uint64_t, o));
+}
+__device__ __forceinline__ void coherent_store4(float* p, const f32x4& v) {
+    coherent_store64(p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}));
+    coherent_store64(p + 2, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}));
+}
+// Four stored state entries as loaded (8 or 16 bytes), widened by widen4.
+__device__ __forceinline__ bf16x4 coherent_load_raw4(const bf16* p) {
+    return __builtin_bit_cast(bf16x4, coherent_load64(p));
+}
+__device__ __forceinline__ f32x4 coherent_load_raw4(const float* p) {
+    const f32x2 lo = __builtin_bit_cast(f32x2, coherent_load64(p));
+    const f32x2 hi = __builtin_bit_cast(f32x2, coherent_load64(p + 2));
+    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ bf16x4 load_raw4(const bf16* p) { return *(const bf16x4*)p; }
+__device__ __forceinline__ f32x4 load_raw4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 widen4(const bf16x4& v) {
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 widen4(const f32x4& v) { return v; }
+// Wait until every memory access this wave issued has completed (stores
+// acknowledged by the point of coherence); the compiler moves no memory
+// access across it.
+__device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Span workgroups.
+//  kModeState  the span's local state from a zero state, and its decay
+//              product (span_state).
+//  kModeScan   y from the state entering the span: as state_pass left it,
+//              or (fuse_pass 1) folded here from the span states of the
+//              earlier spans of the sequence, with the last span then also
+//              writing final_state (span_scan).
+//  kModeFused  both in one launch (fuse_pass 2, batch mode): workgroups
+//              take tickets in span order; each forms its span's local state
+//              and publishes it with a flag, waits for the flags of the
+//              earlier spans of its sequence (all held by earlier tickets, so
+//              running or done), folds their states into the state entering
+//              its span, and writes y.  The last span of a sequence skips the
+//              local state (no later span reads it) and writes final_state.
+template <typename T, int N, int HG, int MODE>
+__global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) void span_kernel(
     KParams p) {
     using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
@@ -422,17 +487,49 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     constexpr int NB = Cf::NB, KN = Cf::KN, EPU = Cf::EPU;
     constexpr int W = 16 / EPU;               // 16-byte units per block row
     constexpr int XI = 4 * W, BI = NB * W;    // load instructions per X / B / C tile
-    __shared__ Smem<T, N, HG, SCAN> sm;
+    constexpr bool SCANL = MODE != kModeState;  // LDS holds the scan buffers
+    __shared__ Smem<T, N, HG, SCANL> sm;
 
-    // XCD-aware order: consecutive logical blocks (same span, neighbouring
-    // head groups, which share B and C) land on the same XCD and its L2.
-    const int hg = SCAN ? p.hg_scan : p.hg_state;
+    const int hg = MODE == kModeState ? p.hg_state : p.hg_scan;
     const int ngrp = (p.H + hg - 1) / hg;
     const int64_t nreal = p.nspan * ngrp * p.npg;
-    const int64_t per = (nreal + kXcds - 1) / kXcds;
-    const int64_t bid = blockIdx.x;
-    const int64_t logical = (bid % kXcds) * per + bid / kXcds;
-    if (logical >= nreal) return;
+    const int tid = threadIdx.x;
+    int64_t logical;
+    uint32_t epoch = 0;
+    if constexpr (MODE == kModeFused) {
+        // Workgroup b serves chain b / sps (one sequence, head group and
+        // column group) and takes the next span of that chain from the
+        // chain's 64-bit header word: the low half counts the chain's
+        // workgroups so far, so a workgroup waits only for spans already
+        // held by running ones; the high half is the chain's launch epoch,
+        // which tags its flags.  The chain's last workgroup resets the count
+        // and advances the epoch for the next launch.
+        const int64_t per_seq = (int64_t)ngrp * p.npg;
+        const int64_t chain = blockIdx.x / p.sps;
+        if (tid == 0) {
+            const uint64_t te = __hip_atomic_fetch_add((uint64_t*)(p.sync + kSyncHeader) + chain, 1ull,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t t = (uint32_t)te, e = (uint32_t)(te >> 32);
+            if (t == (uint32_t)(p.sps - 1))
+                coherent_store64((uint64_t*)(p.sync + kSyncHeader) + chain, (uint64_t)(e + 1) << 32);
+            sm.ticket = t;
+            sm.epoch = e + 1;
+        }
+        block_sync();
+        // (a header not zero-filled before the first launch still maps every
+        // ticket to a span in range)
+        const int64_t kin = sm.ticket % (uint32_t)p.sps;
+        epoch = sm.epoch;
+        const int64_t seq = chain / per_seq;
+        logical = (seq * p.sps + kin) * per_seq + (chain - seq * per_seq);
+    } else {
+        // XCD-aware order: consecutive logical blocks (same span, neighbouring
+        // head groups, which share B and C) land on the same XCD and its L2.
+        const int64_t per = (nreal + kXcds - 1) / kXcds;
+        const int64_t bid = blockIdx.x;
+        logical = (bid % kXcds) * per + bid / kXcds;
+        if (logical >= nreal) return;
+    }
     const int pg = (int)(logical % p.npg);
     const int hgi = (int)((logical / p.npg) % ngrp);
     const int64_t span = logical / ((int64_t)p.npg * ngrp);
@@ -461,7 +558,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
 
     const int pcol0 = pg * kPGroup;
     const int pgw = min(kPGroup, p.P - pcol0);
-    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+    const int wave = wave_id(), lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
     const int q = wave >> 2, w4 = wave & 3;  // quad = head h0 + q; 16-column block w4
     const bool live = q < nh;                // this quad has a head
@@ -503,7 +600,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     };
     // This wave's share of chunk c's C tile (scan).
     auto issue_c = [&](int c, T* __restrict__ cdst) {
-        if constexpr (SCAN)
+        if constexpr (SCANL)
             issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cc0 + c * bcs, dir * GN, wave,
                                                             clen_of(c), N, lane);
     };
@@ -516,47 +613,55 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
         else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
     };
 
-    // The state entering the span, this wave's 16 columns, MFMA result order.
-    // Span scan, separate state pass: read it (the pass replaced each span
-    // state by it).  Span scan, pass folded in (batch mode): fold the span
-    // states of the earlier spans of this sequence in order, from the initial
-    // state, H <- a_j H + S_j in fp32.  The last span of a sequence then also
-    // advances over its last chunk and writes final_state.
-    f32x4 Hs[NB];
     const int kin = (int)(span % (p.sps > 0 ? p.sps : 1));  // span within its sequence
-    const bool write_final = SCAN && p.fuse_pass && p.final_state && kin == p.sps - 1;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool folds = MODE == kModeFused || (MODE == kModeScan && p.fuse_pass);
+    const bool write_final = folds && p.final_state && kin == p.sps - 1;
     // (n, p) of this lane's entry i of state block nb, [N][P] offset
     auto np_off = [&](int nb, int i) -> int64_t {
         return (int64_t)(16 * nb + 4 * g + i) * p.P + 16 * pb + l16;
     };
     const int64_t hseq = ((span - kin) / (p.sps > 0 ? p.sps : 1) * p.H + h) * (int64_t)N * p.P;
-    if (SCAN && active && !p.fuse_pass) {
-        const T* sb = (const T*)p.states + (span * p.H + h) * (int64_t)p.P * N;
+    f32x4 Hs[NB];  // this wave's 16 columns of the state, MFMA result order
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(sb + state_off(pb, nb, lane, NB));
-    }
-    if (SCAN && active && p.fuse_pass) {
-        if (p.init) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Hs[nb][i] = p.init[hseq + np_off(nb, i)];
-        }
-        // (all workgroups fold at once, so this is bound by the bytes read,
-        // not by the latency of the sequential loop)
-        const int64_t sp0 = span - kin;
-        for (int j = 0; j < kin; ++j) {
-            const float a = p.decay[(sp0 + j) * p.H + h];
-            const T* sj = (const T*)p.states + ((sp0 + j) * p.H + h) * (int64_t)p.P * N;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) Hs[nb] = a * Hs[nb] + load4(sj + state_off(pb, nb, lane, NB));
-        }
-    }
+    for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
+    auto state_ptr = [&](int64_t sp) -> T* {
+        return (T*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
+    };
+    // fused kernel: one flag per work item, after the chains' header words
+    uint32_t* const flags = p.sync + kSyncHeader + 2 * (int64_t)p.batch * ngrp * p.npg;
 
-    if constexpr (SCAN) {
+    // The fused kernel's fold of the earlier spans' published states into
+    // the state entering the span, H <- a_j H + S_j in fp32 from the initial
+    // state: the coherent loads go out up to U spans at a time (at most 128
+    // registers of raw state), the first U with the first chunk's tiles.
+    using R4 = typename Vec<T>::x4;
+    constexpr int U = imin_c(kFuseSpans, 128 / (NB * (int)sizeof(T)));
+    float fa[U];
+    R4 fst[U][NB];
+    int64_t fold_at = span - kin;  // next span to fold
+    auto fold_issue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t sj = fold_at + u;
+            if (sj >= span) break;  // the same for the whole wave
+            const T* st = state_ptr(sj);
+            fa[u] = __uint_as_float(coherent_load32((const uint32_t*)&p.decay[sj * p.H + h]));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) fst[u][nb] = coherent_load_raw4(st + state_off(pb, nb, lane, NB));
+        }
+    };
+    auto fold_apply = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (fold_at + u >= span) break;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Hs[nb] = fa[u] * Hs[nb] + widen4(fst[u][nb]);
+        }
+        fold_at += U;
+    };
+
+    if constexpr (SCANL) {
         // mask fragment halves that stay zero: tiles above the diagonal
         // (tb, sb) = (0, 1) and (2, 3)
         for (int i = tid; i < HG * 2 * 64; i += Cf::TH) {
@@ -572,7 +677,8 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) yoff[tb] = (int64_t)(dir * (16 * tb + l16)) * p.ys_t;
 
-    // Software pipeline over the span's chunks; step c:
+    // One pass over the span's chunks, as a software pipeline: the local
+    // state (SCAN false) or y (SCAN true).  Step c:
     //   wait for chunk c's tiles; barrier; (every fourth step) each wave
     //   forms one of the next four chunks' decay factors, barrier, and loads
     //   d_raw of the four after; issue chunk c+1's X and B tiles into the
@@ -581,164 +687,256 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, SCAN>())) 
     // Only loads into LDS are in flight across a step, and the explicit wait
     // at its top covers them; the compiler itself never waits for them (the
     // restrict qualifiers below tell it that the step's LDS reads and the
-    // loads it issues touch different buffers).
-    if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
-    if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
-    issue_xb(0, sm.xs[0][q], sm.bs[0]);
-    issue_c(0, sm.cs);
-    vm_wait<0>();
-    if (w4 < nck) decay_factors<T>(sm.dec[w4][q], sm.dr[0][w4][q][lane], p.d_init, clen_of(w4), lane);
-
-    for (int c = 0; c < nck; ++c) {
-        const bool last = c + 1 == nck;
-        const int buf = c & 1;
-        const int cl = clen_of(c);
-        const Decay& D = sm.dec[c % kWaves][q];
-
-        // After chunk c's loads this wave issued, in an active scan wave,
-        // exactly four y stores (the previous chunk is full), else nothing.
-        if (SCAN && active && c > 0) vm_wait<4>();
-        else vm_wait<0>();
-        block_sync();  // every wave's loads of chunk c are in LDS
-        if (c > 0 && c % kWaves == 0) {
-            // batch c/4: its d_raw was loaded four steps ago
-            const int bb = (c / kWaves) & 1;
-            if (c + w4 < nck)
-                decay_factors<T>(sm.dec[w4][q], sm.dr[bb][w4][q][lane], p.d_init, clen_of(c + w4), lane);
-            block_sync();
-            if (c + kWaves + w4 < nck) issue_d(c + kWaves + w4, sm.dr[bb ^ 1][w4][q]);
+    // loads it issues touch different buffers).  A pass leaves no load in
+    // flight.
+    auto run = [&](auto scan_tag) __attribute__((always_inline)) {
+        constexpr bool SCAN = decltype(scan_tag)::value;
+        if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
+        if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
+        issue_xb(0, sm.xs[0][q], sm.bs[0]);
+        if (SCAN) issue_c(0, sm.cs);
+        if (MODE == kModeFused && SCAN) {
+            // the fused kernel's fold loads go out with the first tiles
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (active) {
+                if (p.init) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Hs[nb][i] = p.init[hseq + np_off(nb, i)];
+                }
+                if (kin > 0) fold_issue();
+            }
         }
+        vm_wait<0>();
+        if (MODE == kModeFused && SCAN && active && kin > 0) {
+            fold_apply();
+            while (fold_at < span) {
+                fold_issue();
+                fold_apply();
+            }
+        }
+        if (w4 < nck) decay_factors<T>(sm.dec[w4][q], sm.dr[0][w4][q][lane], p.d_init, clen_of(w4), lane);
 
-        auto body = [&](const T* __restrict__ xt, const T* __restrict__ bt_tile,
-                        const T* __restrict__ ct, T* __restrict__ xn, T* __restrict__ bn,
-                        T* __restrict__ cn) {
-            if (!last) issue_xb(c + 1, xn, bn);
+        for (int c = 0; c < nck; ++c) {
+            const bool last = c + 1 == nck;
+            const int buf = c & 1;
+            const int cl = clen_of(c);
+            const Decay& D = sm.dec[c % kWaves][q];
 
-            if constexpr (SCAN) {
-                // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
-                X8 cf[4][KN];
+            // After chunk c's loads this wave issued, in an active scan wave,
+            // exactly four y stores (the previous chunk is full), else nothing.
+            if (SCAN && active && c > 0) vm_wait<4>();
+            else vm_wait<0>();
+            block_sync();  // every wave's loads of chunk c are in LDS
+            if (c > 0 && c % kWaves == 0) {
+                // batch c/4: its d_raw was loaded four steps ago
+                const int bb = (c / kWaves) & 1;
+                if (c + w4 < nck)
+                    decay_factors<T>(sm.dec[w4][q], sm.dr[bb][w4][q][lane], p.d_init, clen_of(c + w4), lane);
+                block_sync();
+                if (c + kWaves + w4 < nck) issue_d(c + kWaves + w4, sm.dr[bb ^ 1][w4][q]);
+            }
+
+            auto body = [&](const T* __restrict__ xt, const T* __restrict__ bt_tile,
+                            const T* __restrict__ ct, T* __restrict__ xn, T* __restrict__ bn,
+                            T* __restrict__ cn) {
+                if (!last) issue_xb(c + 1, xn, bn);
+
+                if constexpr (SCAN) {
+                    // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
+                    X8 cf[4][KN];
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
+                    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) cf[tb][kk] = tile_frag<N>(ct, 16 * tb + l16, kk, g);
-                // inter-chunk term y^T = H^T C^T with the state entering chunk c
-                f32x4 ye[4];
-                {
-                    X8 hf[KN];
+                        for (int kk = 0; kk < KN; ++kk) cf[tb][kk] = tile_frag<N>(ct, 16 * tb + l16, kk, g);
+                    // inter-chunk term y^T = H^T C^T with the state entering chunk c
+                    f32x4 ye[4];
+                    {
+                        X8 hf[KN];
 #pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) {
-                        X4 lo, hi = {};
+                        for (int kk = 0; kk < KN; ++kk) {
+                            X4 lo, hi = {};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            lo[i] = cvt<T>(Hs[2 * kk][i]);
-                            if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[2 * kk + 1][i]);
+                            for (int i = 0; i < 4; ++i) {
+                                lo[i] = cvt<T>(Hs[2 * kk][i]);
+                                if (2 * kk + 1 < NB) hi[i] = cvt<T>(Hs[2 * kk + 1][i]);
+                            }
+                            hf[kk] = cat<X8, X4>(lo, hi);
                         }
-                        hf[kk] = cat<X8, X4>(lo, hi);
+#pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) {
+                            ye[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kk = 0; kk < KN; ++kk) ye[tb] = mma(hf[kk], cf[tb][kk], ye[tb]);
+                        }
                     }
+                    // C B^T tiles with t-block >= s-block, 3/3/2/2 per wave, masked
+                    // with this quad's head decay
+                    X8 a[KN];
+                    auto bfrag = [&](int sb) {
+#pragma unroll
+                        for (int kk = 0; kk < KN; ++kk) a[kk] = tile_frag<N>(bt_tile, 16 * sb + l16, kk, g);
+                    };
+                    switch (w4) {
+                        case 0:
+                            bfrag(0);
+                            mask_tile<0, 0>(sm, D, q, lane, a, cf[0]);
+                            mask_tile<1, 0>(sm, D, q, lane, a, cf[1]);
+                            mask_tile<2, 0>(sm, D, q, lane, a, cf[2]);
+                            break;
+                        case 1:
+                            bfrag(1);
+                            mask_tile<1, 1>(sm, D, q, lane, a, cf[1]);
+                            mask_tile<2, 1>(sm, D, q, lane, a, cf[2]);
+                            mask_tile<3, 1>(sm, D, q, lane, a, cf[3]);
+                            break;
+                        case 2:
+                            bfrag(0);
+                            mask_tile<3, 0>(sm, D, q, lane, a, cf[3]);
+                            bfrag(2);
+                            mask_tile<2, 2>(sm, D, q, lane, a, cf[2]);
+                            break;
+                        default:
+                            bfrag(2);
+                            mask_tile<3, 2>(sm, D, q, lane, a, cf[3]);
+                            bfrag(3);
+                            mask_tile<3, 3>(sm, D, q, lane, a, cf[3]);
+                            break;
+                    }
+                    block_sync();  // masked fragments complete, C tile no longer read
+                    if (!last) issue_c(c + 1, cn);
+
+                    // X^T fragments in the K order of the mask tiles:
+                    // tokens 32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3)
+                    X8 xf[2];
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+                        xf[kk] = tok_frag(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, w4, lane);
+                    X8 lf[6];
+#pragma unroll
+                    for (int s = 0; s < 6; ++s) lf[s] = cat<X8, X4>(sm.lf[q][s][0][lane], sm.lf[q][s][1][lane]);
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int tb = 0; tb < 4; ++tb) {
-                        ye[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        // intra-chunk: y^T += X^T L^T (causal fragments only)
+                        f32x4 yi = mma(xf[0], lf[lslot(tb, 0)], z);
+                        if (tb >= 2) yi = mma(xf[1], lf[lslot(tb, 1)], yi);
+                        const int t = 16 * tb + l16;
+                        const float sc = D.fe[t];
+                        f32x4 o;
 #pragma unroll
-                        for (int kk = 0; kk < KN; ++kk) ye[tb] = mma(hf[kk], cf[tb][kk], ye[tb]);
+                        for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
+                        if (active && t < cl) store4_async(yc0 + c * ycs + yoff[tb], o);
                     }
                 }
-                // C B^T tiles with t-block >= s-block, 3/3/2/2 per wave, masked
-                // with this quad's head decay
-                X8 a[KN];
-                auto bfrag = [&](int sb) {
-#pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) a[kk] = tile_frag<N>(bt_tile, 16 * sb + l16, kk, g);
-                };
-                switch (w4) {
-                    case 0:
-                        bfrag(0);
-                        mask_tile<0, 0>(sm, D, q, lane, a, cf[0]);
-                        mask_tile<1, 0>(sm, D, q, lane, a, cf[1]);
-                        mask_tile<2, 0>(sm, D, q, lane, a, cf[2]);
-                        break;
-                    case 1:
-                        bfrag(1);
-                        mask_tile<1, 1>(sm, D, q, lane, a, cf[1]);
-                        mask_tile<2, 1>(sm, D, q, lane, a, cf[2]);
-                        mask_tile<3, 1>(sm, D, q, lane, a, cf[3]);
-                        break;
-                    case 2:
-                        bfrag(0);
-                        mask_tile<3, 0>(sm, D, q, lane, a, cf[3]);
-                        bfrag(2);
-                        mask_tile<2, 2>(sm, D, q, lane, a, cf[2]);
-                        break;
-                    default:
-                        bfrag(2);
-                        mask_tile<3, 2>(sm, D, q, lane, a, cf[3]);
-                        bfrag(3);
-                        mask_tile<3, 3>(sm, D, q, lane, a, cf[3]);
-                        break;
-                }
-                block_sync();  // masked fragments complete, C tile no longer read
-                if (!last) issue_c(c + 1, cn);
 
-                // X^T fragments in the K order of the mask tiles:
-                // tokens 32kk + 4g + (0..3) and 32kk + 16 + 4g + (0..3)
-                X8 xf[2];
+                if (!(SCAN && last) || (SCAN && write_final)) {
+                    // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
+                    const float decay = D.fe[kChunk - 1];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    xf[kk] = tok_frag(xt, 32 * kk + 4 * g, 32 * kk + 16 + 4 * g, w4, lane);
-                X8 lf[6];
+                    for (int nb = 0; nb < NB; ++nb) Hs[nb] *= decay;
 #pragma unroll
-                for (int s = 0; s < 6; ++s) lf[s] = cat<X8, X4>(sm.lf[q][s][0][lane], sm.lf[q][s][1][lane]);
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    for (int kk = 0; kk < kChunk / 32; ++kk) {
+                        const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
+                        const f32x8 ws = ld8(&D.w[s0]);
+                        const X8 xv = tok_frag(xt, s0, s0 + 4, w4, lane);
+                        X8 b, bt[NB];
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    // intra-chunk: y^T += X^T L^T (causal fragments only)
-                    f32x4 yi = mma(xf[0], lf[lslot(tb, 0)], z);
-                    if (tb >= 2) yi = mma(xf[1], lf[lslot(tb, 1)], yi);
-                    const int t = 16 * tb + l16;
-                    const float sc = D.fe[t];
-                    f32x4 o;
+                        for (int nb = 0; nb < NB; ++nb) bt[nb] = tok_frag(bt_tile, s0, s0 + 4, nb, lane);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
-                    if (active && t < cl) store4_async(yc0 + c * ycs + yoff[tb], o);
+                        for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) Hs[nb] = mma(bt[nb], b, Hs[nb]);
+                    }
                 }
-            }
+                if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
+            };
+            body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.xs[buf ^ 1][q], sm.bs[buf ^ 1], sm.cs);
+        }
+    };
 
-            if (!(SCAN && last) || write_final) {
-                // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
-                const float decay = D.fe[kChunk - 1];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) Hs[nb] *= decay;
-#pragma unroll
-                for (int kk = 0; kk < kChunk / 32; ++kk) {
-                    const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
-                    const f32x8 ws = ld8(&D.w[s0]);
-                    const X8 xv = tok_frag(xt, s0, s0 + 4, w4, lane);
-                    X8 b, bt[NB];
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) bt[nb] = tok_frag(bt_tile, s0, s0 + 4, nb, lane);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) Hs[nb] = mma(bt[nb], b, Hs[nb]);
-                }
-            }
-            if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
-        };
-        body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.xs[buf ^ 1][q], sm.bs[buf ^ 1], sm.cs);
-    }
-
-    if (write_final && active) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p.final_state[hseq + np_off(nb, i)] = Hs[nb][i];
-    }
-    if (!SCAN) {
+    if constexpr (MODE == kModeState) {
+        run(std::false_type{});
         if (active) {
-            T* sb = (T*)p.states + (span * p.H + h) * (int64_t)p.P * N;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) store4(sb + state_off(pb, nb, lane, NB), Hs[nb]);
+            for (int nb = 0; nb < NB; ++nb) store4(state_ptr(span) + state_off(pb, nb, lane, NB), Hs[nb]);
         }
         if (pg == 0 && w4 == 0 && live && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
+        return;
+    }
+
+    if constexpr (MODE == kModeFused) {
+        if (kin + 1 < p.sps) {
+            // the span's local state and decay, published for the later spans
+            run(std::false_type{});
+            if (active) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    coherent_store4(state_ptr(span) + state_off(pb, nb, lane, NB), Hs[nb]);
+            }
+            if (w4 == 0 && live && lane == 0)
+                coherent_store32((uint32_t*)&p.decay[span * p.H + h], __float_as_uint(fexp2(logdec2)));
+            drain_vm();    // this wave's stores have reached the point of coherence
+            block_sync();  // so have every wave's; the pass's LDS is free again
+            if (tid == 0) coherent_store32(flags + logical, epoch);
+        }
+        if (kin > 0) {
+            // Wait for the flags of spans 0 .. kin-1 of this sequence (same
+            // head group and column group), lane j of wave 0 polling span j.
+            // The wait is bounded: flags that never come (a header not
+            // zero-filled before first use) are counted in the header and
+            // the fold goes on without them.
+            if (wave == 0) {
+                const uint32_t* f = flags + ((span - kin + (lane < kin ? lane : 0)) * ngrp + hgi) * p.npg + pg;
+                uint32_t budget = kSpinBudget;
+                while (!__all(lane >= kin || coherent_load32(f) == epoch)) {
+                    if (--budget == 0) {
+                        if (lane == 0)
+                            __hip_atomic_fetch_add(p.sync + kSyncTimeouts, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            block_sync();
+        }
+    }
+
+    if constexpr (MODE == kModeScan) {
+        // (span_scan) the state entering the span: as state_pass left it in
+        // place of the span state, or folded here span by span
+        if (active) {
+            if (!folds) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(state_ptr(span) + state_off(pb, nb, lane, NB));
+            } else {
+                if (p.init) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Hs[nb][i] = p.init[hseq + np_off(nb, i)];
+                }
+                for (int64_t sj = span - kin; sj < span; ++sj) {
+                    const float a = p.decay[sj * p.H + h];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        Hs[nb] = a * Hs[nb] + load4(state_ptr(sj) + state_off(pb, nb, lane, NB));
+                }
+            }
+        }
+    }
+
+    if constexpr (SCANL) {
+        run(std::true_type{});
+        if (write_final && active) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p.final_state[hseq + np_off(nb, i)] = Hs[nb][i];
+        }
     }
 }
 
@@ -876,43 +1074,44 @@ __global__ __launch_bounds__(kTab) void span_table_kernel(const int32_t* cu, int
     for (int64_t k = (int64_t)carry_off + tid; k < nspan; k += kTab) table[k] = make_int4(-1, 0, 0, 0);
 }
 
-template <typename T, int N, int HG, bool SCAN>
+template <typename T, int N, int HG, int MODE>
 hipError_t launch_span_hg(const KParams& p, int hg, hipStream_t s) {
     const int64_t nreal = p.nspan * ((p.H + hg - 1) / hg) * p.npg;
     if (nreal == 0) return hipSuccess;
-    const int64_t per = (nreal + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((span_kernel<T, N, HG, SCAN>), dim3((unsigned)(per * kXcds)),
-                       dim3(kThreads * HG), 0, s, p);
+    // the fused kernel takes one ticket per workgroup: exactly nreal of them
+    const int64_t grid = MODE == kModeFused ? nreal : (nreal + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((span_kernel<T, N, HG, MODE>), dim3((unsigned)grid), dim3(kThreads * HG), 0,
+                       s, p);
     return hipGetLastError();
 }
 
-// Instantiated for 1, 2 and 4 heads per workgroup, up to the most the kernel
+// Instantiated for 1 and 2 heads per workgroup, up to the most the kernel
 // can carry at this d_state.
-template <typename T, int N, bool SCAN>
+template <typename T, int N, int MODE>
 hipError_t launch_span_t(const KParams& p, hipStream_t s) {
-    constexpr int MAXH = SCAN ? heads_scan(N, sizeof(T)) : heads_state(N, sizeof(T));
-    const int hg = SCAN ? p.hg_scan : p.hg_state;
-    if (hg == 1) return launch_span_hg<T, N, 1, SCAN>(p, 1, s);
-    if (hg == 2 && MAXH >= 2) return launch_span_hg<T, N, (MAXH >= 2 ? 2 : 1), SCAN>(p, 2, s);
+    constexpr int MAXH = MODE != kModeState ? heads_scan(N, sizeof(T)) : heads_state(N, sizeof(T));
+    const int hg = MODE != kModeState ? p.hg_scan : p.hg_state;
+    if (hg == 1) return launch_span_hg<T, N, 1, MODE>(p, 1, s);
+    if (hg == 2 && MAXH >= 2) return launch_span_hg<T, N, (MAXH >= 2 ? 2 : 1), MODE>(p, 2, s);
     return hipErrorInvalidValue;
 }
 
-template <bool SCAN>
+template <int MODE>
 hipError_t launch_span(const KParams& p, int dtype, int N, hipStream_t s) {
     if (dtype == 1) {
         switch (N) {
-            case 16: return launch_span_t<bf16, 16, SCAN>(p, s);
-            case 32: return launch_span_t<bf16, 32, SCAN>(p, s);
-            case 64: return launch_span_t<bf16, 64, SCAN>(p, s);
-            case 128: return launch_span_t<bf16, 128, SCAN>(p, s);
-            case 256: return launch_span_t<bf16, 256, SCAN>(p, s);
+            case 16: return launch_span_t<bf16, 16, MODE>(p, s);
+            case 32: return launch_span_t<bf16, 32, MODE>(p, s);
+            case 64: return launch_span_t<bf16, 64, MODE>(p, s);
+            case 128: return launch_span_t<bf16, 128, MODE>(p, s);
+            case 256: return launch_span_t<bf16, 256, MODE>(p, s);
         }
     } else {
         switch (N) {
-            case 16: return launch_span_t<float, 16, SCAN>(p, s);
-            case 32: return launch_span_t<float, 32, SCAN>(p, s);
-            case 64: return launch_span_t<float, 64, SCAN>(p, s);
-            case 128: return launch_span_t<float, 128, SCAN>(p, s);
+            case 16: return launch_span_t<float, 16, MODE>(p, s);
+            case 32: return launch_span_t<float, 32, MODE>(p, s);
+            case 64: return launch_span_t<float, 64, MODE>(p, s);
+            case 128: return launch_span_t<float, 128, MODE>(p, s);
         }
     }
     return hipErrorInvalidValue;
@@ -958,11 +1157,12 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T, int
 }
 
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s) {
-    return launch_span<false>(p, dtype, N, s);
+    return launch_span<kModeState>(p, dtype, N, s);
 }
 
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s) {
-    return launch_span<true>(p, dtype, N, s);
+    return p.fuse_pass == 2 ? launch_span<kModeFused>(p, dtype, N, s)
+                            : launch_span<kModeScan>(p, dtype, N, s);
 }
 
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s) {

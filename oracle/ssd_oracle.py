@@ -4,7 +4,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The HIP library never calls it and
 shares no code with it.
 
-Sources (the pages this build is written from):
+Sources (the pages the method is taken from):
 
 * [M2-LaCT] "Mamba-2架构与LaCT并行计算技术解析" (jsqmd.com).
   §1.1 gives the per-head recurrence: d = softplus(d_raw + d_init),
@@ -35,7 +35,7 @@ What is here:
   pairs used to pass state between chunks or shards ([MindSpeed-CP] §三.2).
 * ``rel_err``             -- max|a-b| / max|b|, the parity metric.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 d_init is added before softplus; softplus uses the stable form with no
 threshold; decay is exp(-d) (no separate learned A, no D skip, no gate);
 y_t reads the state *after* token t's update; B_t^T X_t is the outer product

@@ -122,15 +122,37 @@ def test_binding_rejects_cpu_mismatch(m):
 
 
 def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
-    """Batch mode with at most 16 spans per sequence folds the state pass
-    into span_scan; packed sequences and longer ones keep the pass kernel."""
+    """Batch mode with 1..16 spans per sequence folds the state pass into
+    span_scan; packed sequences, longer ones and empty ones keep the three
+    launches; SSD_FUSE_PASS forces any of the three plans in batch mode."""
     monkeypatch.delenv("SSD_FUSE_PASS", raising=False)
     monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
-    layer = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128))
+    layer_dims = m.make_dims(2, 2048, 24, 64, 128)
+    layer = m.ssd_fwd_plan(layer_dims)
     assert layer.chunks_per_span == 4 and layer.fused_pass == 1
     long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 17, 2, 64, 128))
     assert long.fused_pass == 0
     varlen = m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3))
     assert varlen.fused_pass == 0
-    monkeypatch.setenv("SSD_FUSE_PASS", "0")
-    assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).fused_pass == 0
+    assert m.ssd_fwd_plan(m.make_dims(2, 0, 2, 64, 128)).fused_pass == 0
+    for forced in (0, 1, 2):
+        monkeypatch.setenv("SSD_FUSE_PASS", str(forced))
+        assert m.ssd_fwd_plan(layer_dims).fused_pass == forced
+        assert m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3)).fused_pass == 0
+
+
+def test_workspace_header_in_every_plan(m, monkeypatch):
+    """Every plan reserves the 256-byte header at the start of the
+    workspace; the fused plan adds one 8-byte ticket/epoch word per chain
+    (sequence, head group, column group) and one 4-byte flag per
+    workgroup."""
+    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
+    sizes = {}
+    for forced in (0, 1, 2):
+        monkeypatch.setenv("SSD_FUSE_PASS", str(forced))
+        sizes[forced] = m.ssd_fwd_workspace_bytes(m.make_dims(2, 2048, 24, 64, 128))
+    assert sizes[0] == sizes[1]
+    chains = 2 * 24  # sequences x heads x one column group
+    nwg = chains * (2048 // 64 // 4)  # x spans per sequence
+    assert sizes[2] - sizes[0] == -(-(chains * 8 + nwg * 4) // 256) * 256
+    assert m.ssd_fwd_workspace_bytes(m.make_dims(2, 0, 2, 64, 128)) >= 256

@@ -135,6 +135,36 @@ def test_shapes(ssd, shape, dtype, reverse):
     check(ssd, p, reverse, label=f"{shape} {dtype} rev={reverse}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("reverse", [False, True])
+def test_shapes_fused_launch(ssd, shape, dtype, reverse, monkeypatch):
+    """The single fused launch, one chunk per span (so every sequence longer
+    than 64 tokens hands states between workgroups), on every shape."""
+    b, L, H, P, N, G = shape
+    if dtype == "f32" and N > 128:
+        pytest.skip("fp32 path is built for d_state <= 128")
+    if (L + 63) // 64 > 16:
+        pytest.skip("more than 16 spans per sequence")
+    monkeypatch.setenv("SSD_FUSE_PASS", "2")
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "1")
+    p = random_problem(103, b, L, H, P, N, ngroups=G, dtype=dtype, init_scale=0.5,
+                       d_init=-2.0)
+    check(ssd, p, reverse, label=f"fused {shape} {dtype} rev={reverse}")
+
+
+@pytest.mark.parametrize("fuse", ["1", "2"])
+def test_two_heads_per_scan_workgroup(ssd, fuse, monkeypatch):
+    """Span workgroups carrying two heads (one quad of waves each) in the
+    folding and the fused plans."""
+    monkeypatch.setenv("SSD_FUSE_PASS", fuse)
+    monkeypatch.setenv("SSD_HEADS_SCAN", "2")
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+    p = random_problem(107, 2, 700, 4, 64, 64, dtype="bf16", init_scale=0.5)
+    check(ssd, p, False, label=f"hg2 fuse={fuse}")
+    check(ssd, p, True, label=f"hg2 fuse={fuse} rev")
+
+
 @pytest.mark.parametrize("reverse", [False, True])
 def test_varlen_ragged(ssd, reverse):
     lens = [1, 63, 64, 65, 0, 200, 129, 7, 0, 640]
@@ -169,12 +199,13 @@ def test_span_length_invariance(ssd, k, monkeypatch):
     check(ssd, q, True, label=f"K={k} varlen rev f32")
 
 
-@pytest.mark.parametrize("fuse", ["0", "1"])
+@pytest.mark.parametrize("fuse", ["0", "1", "2"])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
-    """Both ways of handing the state from span to span match the oracle: the
-    separate state_pass kernel, and span_scan folding the earlier span states
-    of its sequence itself (which also writes final_state)."""
+    """Every way of handing the state from span to span matches the oracle:
+    the separate state_pass kernel (0), span_scan folding the earlier span
+    states of its sequence itself (1), and the single fused launch whose
+    workgroups hand span states to each other (2)."""
     monkeypatch.setenv("SSD_FUSE_PASS", fuse)
     monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
     p = random_problem(151, 2, 1000, 3, 64, 128, dtype="bf16", init_scale=0.5)
@@ -184,6 +215,55 @@ def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
     check(ssd, p, reverse, label=f"fuse={fuse} bf16")
     q = random_problem(157, 3, 500, 2, 32, 64, dtype="f32", init_scale=0.5)
     check(ssd, q, reverse, label=f"fuse={fuse} f32")
+
+
+def _sync_words(ws, chains):
+    """Count of timed-out flag waits (header word 2) and each chain's 64-bit
+    ticket/epoch word (after the 256-byte header), as (count, epoch) pairs."""
+    timeouts = int(ws[8:12].view(torch.int32).item())
+    words = ws[256:256 + 8 * chains].view(torch.int32).view(chains, 2).cpu().tolist()
+    return timeouts, [tuple(w) for w in words]
+
+
+def test_fused_handoff_repeated_calls(ssd, monkeypatch):
+    """The fused launch hands span states between workgroups through the
+    workspace, with flags tagged by a per-launch epoch.  Alternate two input
+    sets on one workspace: every call must reproduce its input set's first
+    result bit for bit (a state left by the other set's call would change
+    it), agree with the three-launch plan, and leave every chain's word at
+    count 0, epoch = number of fused launches, with no timed-out waits.
+    1024 workgroups of 16 spans per sequence: more than the GPU holds at
+    once."""
+    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
+    monkeypatch.setenv("SSD_FUSE_PASS", "2")
+    probs = [random_problem(seed, 8, 4096, 8, 64, 128, dtype="bf16", init_scale=0.5)
+             for seed in (161, 163)]
+    devs = [to_dev(p) for p in probs]
+    calls = [ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+             for d in devs]
+    plan = ssd.ssd_fwd_plan(calls[0].dims)
+    assert plan.fused_pass == 2 and plan.nspan == 8 * 16
+    ws = calls[0].workspace
+    calls = [ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"],
+                         workspace=ws) for d in devs]
+    first = []
+    for i in range(24):
+        y, f = calls[i % 2].run()
+        y, f = y.clone(), f.clone()
+        if i < 2:
+            first.append((y, f))
+        else:
+            y0, f0 = first[i % 2]
+            assert torch.equal(y, y0) and torch.equal(f, f0), f"call {i} differs from call {i % 2}"
+    torch.cuda.synchronize()
+    assert _sync_words(ws, 8 * 8) == (0, [(0, 24)] * 64)
+    monkeypatch.setenv("SSD_FUSE_PASS", "0")
+    for k, d in enumerate(devs):
+        y3, f3 = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+        torch.cuda.synchronize()
+        y0, f0 = first[k]
+        assert O.rel_err(y0.float().cpu(), y3.float().cpu()) <= 1e-2
+        assert O.rel_err(f0.cpu(), f3.cpu()) <= 1e-2
 
 
 def test_empty_sequence_keeps_init(ssd):
