@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -93,7 +93,8 @@ size_t ssd_fwd_workspace_bytes(const ssd_dims* dims);
  *   reverse     0 = causal, 1 = anti-causal within each sequence
  *   y           output [b, L, H, P] of dtype, element (bi, l, h, p) at
  *               y + (bi*L + l)*y_token_stride + h*y_head_stride + p;
- *               strides in elements, multiples of 16 bytes
+ *               strides in elements, multiples of 16 bytes; the token
+ *               stride at most 2^24
  *   final_state output [S, H, N, P] float32, or NULL to skip
  *   workspace   device scratch of at least ssd_fwd_workspace_bytes(dims)
  *               bytes, 256-byte aligned.  Zero-fill it once before its
@@ -135,7 +136,14 @@ typedef struct ssd_plan_info {
                                   other); STATE and PASS launch nothing.
                                   1 is the default in batch mode with 1..16
                                   spans per sequence, else 0; the environment
-                                  variable SSD_FUSE_PASS=0/1/2 forces one.  */
+                                  variable SSD_FUSE_PASS=0/1/2 forces one.
+                                  Always 0 with head-wave kernels.          */
+    int32_t head_wave;         /* 1: head-wave kernels (one wave computes every
+                                  product of one head for cols_per_wave
+                                  headdim columns); 0: span kernels (four
+                                  waves per head, 16 columns each)          */
+    int32_t heads_per_wg;      /* heads sharing one workgroup's B / C tiles  */
+    int32_t cols_per_wave;     /* headdim columns one wave computes          */
 } ssd_plan_info;
 
 /* Fills *out for these sizes; returns the status ssd_fwd's size checks

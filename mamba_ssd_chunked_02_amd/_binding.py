@@ -49,6 +49,9 @@ class SsdPlanInfo(ctypes.Structure):
         ("nspan", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
         ("fused_pass", ctypes.c_int32),
+        ("head_wave", ctypes.c_int32),
+        ("heads_per_wg", ctypes.c_int32),
+        ("cols_per_wave", ctypes.c_int32),
     ]
 
 

@@ -27,6 +27,8 @@ struct Plan {
     int32_t hg_scan = 1;    // heads per span_scan workgroup
     int32_t fuse = 0;       // 1: span_scan forms incoming states (no state_pass
                             // launch); 2: one fused launch does every stage
+    int32_t hw_npb = 0;     // head-wave kernels: 16-column blocks per wave;
+                            // 0 = span kernels
     int64_t nspan = 0;      // span slots
     size_t off_sync = 0, off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
     size_t total = 0;
@@ -45,6 +47,46 @@ int32_t choose_k(int64_t nch, int64_t groups) {
     int32_t K = 4;
     while (K < 8 && ceil_div(nch, K) * groups >= 4096) K *= 2;
     return K;
+}
+
+// Head-wave kernels (bf16, d_state 64 / 128): a head's work for a chunk in
+// one wave per 32 headdim columns (npb 2) or 64 (npb 4, d_state 64 only).
+// Their per-chunk pipeline is cheaper than the span kernels' but needs long
+// spans to pay for the state pass, so they serve problems with at least
+// 8192 chunk-head-column-group work items (on one MI355X the span kernels
+// are faster below that).  Spans: the longest of 32, 16, ... chunks that
+// still give >= 2048 waves; 4 heads per workgroup at d_state 128 (they share
+// the B / C tiles and the causal C B^T), 2 at d_state 64.
+// SSD_KERNEL=span|hw forces a family; SSD_HW_NPB, SSD_HW_HEADS and
+// SSD_SPAN_CHUNKS override the shape (tuning sweeps).
+bool choose_hw(int64_t nch, int64_t heads, int64_t npg, int32_t hpg, int32_t N, int32_t* K,
+               int32_t* npb, int32_t* hg) {
+    const char* kf = getenv("SSD_KERNEL");
+    if (kf && strcmp(kf, "span") == 0) return false;
+    const bool forced = kf && strcmp(kf, "hw") == 0;
+    if (!forced && nch * heads * npg < 8192) return false;
+    int32_t b = 2;
+    auto waves = [&](int32_t k) { return ceil_div(nch, k) * heads * npg * (4 / b); };
+    int32_t k = 32;
+    while (k > 1 && waves(k) < 2048) k /= 2;
+    int32_t g = N >= 128 ? 4 : 2;
+    while (hpg % g) g /= 2;
+    if (const char* e = getenv("SSD_HW_NPB")) {
+        const int v = atoi(e);
+        if (v == 2 || (v == 4 && N <= 64)) b = v;
+    }
+    if (const char* e = getenv("SSD_HW_HEADS")) {
+        const int v = atoi(e);
+        if ((v == 1 || v == 2 || v == 4) && hpg % v == 0) g = v;
+    }
+    if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 64) k = v;
+    }
+    *K = k;
+    *npb = b;
+    *hg = g;
+    return true;
 }
 
 // Heads per workgroup: `dflt` unless the named environment variable asks
@@ -84,6 +126,16 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
                                           : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);
     pl->K = choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg);
+    // Large bf16 problems with d_state 64 or 128 run the head-wave kernels.
+    if (d->dtype == SSD_BF16 && (d->d_state == 64 || d->d_state == 128)) {
+        int32_t K, npb, hg;
+        if (choose_hw(nch_bound, d->nheads, pl->npg, hpg, d->d_state, &K, &npb, &hg) &&
+            ssd::hw_supported(d->dtype, d->d_state, hg, npb)) {
+            pl->K = K;
+            pl->hw_npb = npb;
+            pl->hg_state = pl->hg_scan = hg;
+        }
+    }
     if (d->nseq > 0) {
         pl->sps = 0;
         pl->nspan = ceil_div(T, (int64_t)kChunk * pl->K) + d->nseq;
@@ -102,7 +154,7 @@ int make_plan(const ssd_dims* d, Plan* pl) {
         if (const char* e = getenv("SSD_FUSE_PASS")) {
             if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) pl->fuse = e[0] - '0';
         }
-        if (pl->sps == 0) pl->fuse = 0;
+        if (pl->sps == 0 || pl->hw_npb) pl->fuse = 0;  // head-wave: three launches
         if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) pl->fuse = 1;
     }
     // The header sits at the start of every plan's workspace; the fused
@@ -188,6 +240,9 @@ int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out) {
     out->nspan = pl.nspan;
     out->workspace_bytes = pl.total;
     out->fused_pass = pl.fuse;
+    out->heads_per_wg = pl.hg_scan;
+    out->cols_per_wave = pl.hw_npb ? 16 * pl.hw_npb : 16;
+    out->head_wave = pl.hw_npb ? 1 : 0;
     return SSD_OK;
 }
 
@@ -220,6 +275,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y)) return SSD_ERR_ALIGN;
     if (y_token_stride % per_unit != 0 || y_head_stride % per_unit != 0) return SSD_ERR_ALIGN;
     if (y_token_stride < 0 || y_head_stride < 0) return SSD_ERR_SHAPE;
+    if (y_token_stride > ((int64_t)1 << 24)) return SSD_ERR_SHAPE;
     if (((uintptr_t)init_state & 3u) || ((uintptr_t)final_state & 3u)) return SSD_ERR_ALIGN;
     if (pl.total > 0) {
         if (!workspace || workspace_bytes < pl.total) return SSD_ERR_WORKSPACE;
@@ -263,6 +319,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.hg_scan = pl.hg_scan;
     p.reverse = reverse;
     p.fuse_pass = pl.fuse;
+    p.hw_npb = pl.hw_npb;
     p.sync = (uint32_t*)(ws + pl.off_sync);
     p.d_init = d_init;
 
@@ -279,7 +336,8 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
         }
     }
     if ((mask & SSD_STAGE_STATE) && pl.fuse != 2) {
-        e = ssd::launch_span_state(p, d.dtype, d.d_state, s);
+        e = pl.hw_npb ? ssd::launch_hw_state(p, d.d_state, s)
+                      : ssd::launch_span_state(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     if ((mask & SSD_STAGE_PASS) && !pl.fuse) {
@@ -287,7 +345,8 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     if (mask & SSD_STAGE_SCAN) {
-        e = ssd::launch_span_scan(p, d.dtype, d.d_state, s);
+        e = pl.hw_npb ? ssd::launch_hw_scan(p, d.d_state, s)
+                      : ssd::launch_span_scan(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     return SSD_OK;

@@ -44,6 +44,8 @@ struct KParams {
                             // forms each span's incoming state from the span
                             // states itself and writes final_state (no
                             // state_pass).  2: one fused launch does all.
+    int32_t hw_npb;         // head-wave kernels: 16-column blocks per wave (2 or
+                            // 4); 0 = span kernels
     uint32_t* sync;         // workspace header; for fuse_pass 2 followed by one
                             // 64-bit ticket/epoch word per chain and one flag
                             // per workgroup
@@ -71,6 +73,13 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s);
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s);
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
+
+// Head-wave kernels (ssd_hw_kernels.hip): bf16, d_state 64 or 128; hg heads
+// per workgroup (1, 2, 4), npb 16-column blocks per wave (2, 4).
+bool hw_supported(int dtype, int N, int hg, int npb);
+size_t hw_lds_bytes(int N, int hg, int npb, bool scan);
+hipError_t launch_hw_state(const KParams& p, int N, hipStream_t s);
+hipError_t launch_hw_scan(const KParams& p, int N, hipStream_t s);
 
 // Most heads one span workgroup can carry for this d_state.
 int span_max_heads(int dtype, int N, bool scan);

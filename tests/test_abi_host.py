@@ -127,6 +127,7 @@ def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
     launches; SSD_FUSE_PASS forces any of the three plans in batch mode."""
     monkeypatch.delenv("SSD_FUSE_PASS", raising=False)
     monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
+    monkeypatch.setenv("SSD_KERNEL", "span")
     layer_dims = m.make_dims(2, 2048, 24, 64, 128)
     layer = m.ssd_fwd_plan(layer_dims)
     assert layer.chunks_per_span == 4 and layer.fused_pass == 1
@@ -147,6 +148,7 @@ def test_workspace_header_in_every_plan(m, monkeypatch):
     (sequence, head group, column group) and one 4-byte flag per
     workgroup."""
     monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
+    monkeypatch.setenv("SSD_KERNEL", "span")
     sizes = {}
     for forced in (0, 1, 2):
         monkeypatch.setenv("SSD_FUSE_PASS", str(forced))
@@ -156,3 +158,26 @@ def test_workspace_header_in_every_plan(m, monkeypatch):
     nwg = chains * (2048 // 64 // 4)  # x spans per sequence
     assert sizes[2] - sizes[0] == -(-(chains * 8 + nwg * 4) // 256) * 256
     assert m.ssd_fwd_workspace_bytes(m.make_dims(2, 0, 2, 64, 128)) >= 256
+
+def test_plan_head_wave_kernels(m, monkeypatch):
+    """Large bf16 problems with d_state 64 / 128 run the head-wave kernels
+    with three launches and long spans; small ones, fp32, other d_state
+    values and SSD_KERNEL=span keep the span kernels; SSD_KERNEL=hw forces
+    the head-wave kernels."""
+    for v in ("SSD_FUSE_PASS", "SSD_SPAN_CHUNKS", "SSD_KERNEL", "SSD_HW_NPB", "SSD_HW_HEADS"):
+        monkeypatch.delenv(v, raising=False)
+    varlen = m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16))
+    assert (varlen.head_wave, varlen.chunks_per_span, varlen.cols_per_wave, varlen.heads_per_wg,
+            varlen.fused_pass) == (1, 16, 32, 4, 0)
+    bidir = m.ssd_fwd_plan(m.make_dims(1, 1 << 20, 8, 192, 64))
+    assert (bidir.head_wave, bidir.chunks_per_span, bidir.cols_per_wave, bidir.heads_per_wg) == (1, 32, 32, 2)
+    wide = m.ssd_fwd_plan(m.make_dims(1, 8192, 80, 64, 128))
+    assert (wide.head_wave, wide.chunks_per_span) == (1, 8)
+    assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).head_wave == 0   # layer: span kernels
+    assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, dtype=0)).head_wave == 0
+    assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 32)).head_wave == 0
+    monkeypatch.setenv("SSD_KERNEL", "hw")
+    small = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128))
+    assert small.head_wave == 1 and small.fused_pass == 0
+    monkeypatch.setenv("SSD_KERNEL", "span")
+    assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16)).head_wave == 0

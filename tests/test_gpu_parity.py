@@ -123,16 +123,81 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("family", ["default", "span", "hw"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("reverse", [False, True])
-def test_shapes(ssd, shape, dtype, reverse):
+def test_shapes(ssd, shape, dtype, reverse, family, monkeypatch):
+    """Every shape through the default kernels, through the span kernels
+    alone and with the head-wave kernels forced (they take bf16 problems
+    with d_state 64 / 128; others keep the span kernels)."""
     b, L, H, P, N, G = shape
     if dtype == "f32" and N > 128:
         pytest.skip("fp32 path is built for d_state <= 128")
+    if family != "default":
+        monkeypatch.setenv("SSD_KERNEL", family)
     p = random_problem(101, b, L, H, P, N, ngroups=G, dtype=dtype, init_scale=0.5,
                        d_init=-2.0)
-    check(ssd, p, reverse, label=f"{shape} {dtype} rev={reverse}")
+    check(ssd, p, reverse, label=f"{shape} {dtype} rev={reverse} {family}")
+
+
+HW_SHAPES = [
+    # (batch, seqlen, nheads, headdim, d_state, ngroups)
+    (2, 700, 4, 64, 128, 1),
+    (1, 333, 8, 128, 64, 2),
+    (1, 130, 4, 80, 128, 1),
+    (3, 64, 4, 192, 64, 1),
+]
+
+
+@pytest.mark.parametrize("heads", ["1", "2", "4"])
+@pytest.mark.parametrize("npb", ["2", "4"])
+@pytest.mark.parametrize("k", ["1", "3", "8"])
+@pytest.mark.parametrize("shape", HW_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_head_wave_variants(ssd, shape, heads, npb, k, monkeypatch):
+    """Every head-wave workgroup shape (1 / 2 / 4 heads, waves of 64 or 32
+    headdim columns) at several span lengths, forward and reverse, with a
+    partial column group (headdim 80) and two B / C groups."""
+    monkeypatch.setenv("SSD_KERNEL", "hw")
+    monkeypatch.setenv("SSD_HW_HEADS", heads)
+    monkeypatch.setenv("SSD_HW_NPB", npb)
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", k)
+    b, L, H, P, N, G = shape
+    if npb == "4" and N > 64:
+        pytest.skip("full-width head waves are built for d_state <= 64")
+    p = random_problem(211, b, L, H, P, N, ngroups=G, dtype="bf16", init_scale=0.5)
+    d = to_dev(p)
+    call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+    plan = ssd.ssd_fwd_plan(call.dims)
+    assert plan.head_wave == 1 and plan.heads_per_wg == int(heads)
+    assert plan.cols_per_wave == 16 * int(npb) and plan.chunks_per_span == int(k)
+    for rev in (False, True):
+        check(ssd, p, rev, label=f"hw {shape} hg={heads} npb={npb} K={k} rev={rev}")
+
+
+@pytest.mark.parametrize("d_init", [-9.0, -3.0, 1.0])
+@pytest.mark.parametrize("N", [64, 128])
+def test_head_wave_rescaled_state(ssd, d_init, N, monkeypatch):
+    """The rescaled state across long spans: weak decay (no restart in 16
+    chunks), medium decay (the running scale restarts every few chunks) and
+    strong decay (every chunk restarts), forward and reverse."""
+    monkeypatch.setenv("SSD_KERNEL", "hw")
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "16")
+    p = random_problem(227, 1, 1500, 4, 64, N, dtype="bf16", init_scale=0.5, d_init=d_init,
+                       d_raw_scale=2.0)
+    for rev in (False, True):
+        check(ssd, p, rev, label=f"hw rescale d_init={d_init} N={N} rev={rev}")
+
+
+@pytest.mark.parametrize("npb", ["2", "4"])
+def test_head_wave_varlen(ssd, npb, monkeypatch):
+    monkeypatch.setenv("SSD_KERNEL", "hw")
+    monkeypatch.setenv("SSD_HW_NPB", npb)
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+    lens = [1, 63, 64, 65, 0, 200, 129, 7, 0, 640]
+    p = random_problem(223, 1, 0, 4, 64, 128, dtype="bf16", lengths=lens, init_scale=0.3)
+    for rev in (False, True):
+        check(ssd, p, rev, label=f"hw varlen npb={npb} rev={rev}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -141,6 +206,7 @@ def test_shapes(ssd, shape, dtype, reverse):
 def test_shapes_fused_launch(ssd, shape, dtype, reverse, monkeypatch):
     """The single fused launch, one chunk per span (so every sequence longer
     than 64 tokens hands states between workgroups), on every shape."""
+    monkeypatch.setenv("SSD_KERNEL", "span")
     b, L, H, P, N, G = shape
     if dtype == "f32" and N > 128:
         pytest.skip("fp32 path is built for d_state <= 128")
@@ -157,6 +223,7 @@ def test_shapes_fused_launch(ssd, shape, dtype, reverse, monkeypatch):
 def test_two_heads_per_scan_workgroup(ssd, fuse, monkeypatch):
     """Span workgroups carrying two heads (one quad of waves each) in the
     folding and the fused plans."""
+    monkeypatch.setenv("SSD_KERNEL", "span")
     monkeypatch.setenv("SSD_FUSE_PASS", fuse)
     monkeypatch.setenv("SSD_HEADS_SCAN", "2")
     monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
@@ -206,6 +273,7 @@ def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
     the separate state_pass kernel (0), span_scan folding the earlier span
     states of its sequence itself (1), and the single fused launch whose
     workgroups hand span states to each other (2)."""
+    monkeypatch.setenv("SSD_KERNEL", "span")
     monkeypatch.setenv("SSD_FUSE_PASS", fuse)
     monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
     p = random_problem(151, 2, 1000, 3, 64, 128, dtype="bf16", init_scale=0.5)
@@ -234,6 +302,7 @@ def test_fused_handoff_repeated_calls(ssd, monkeypatch):
     count 0, epoch = number of fused launches, with no timed-out waits.
     1024 workgroups of 16 spans per sequence: more than the GPU holds at
     once."""
+    monkeypatch.setenv("SSD_KERNEL", "span")
     monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
     monkeypatch.setenv("SSD_FUSE_PASS", "2")
     probs = [random_problem(seed, 8, 4096, 8, 64, 128, dtype="bf16", init_scale=0.5)
