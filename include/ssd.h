@@ -1,5 +1,5 @@
 /*
- * libssd -- Mamba-2 SSD selective state-space scan, forward pass, on one
+ * libssd -- Mamba-2 SSD selective state-space scan, forward and backward, on one
  * MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ types, no
  * exceptions across the boundary.
  *
@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -173,6 +173,57 @@ int ssd_fwd_stages(uint32_t stage_mask, const ssd_dims* dims,
                    float* final_state,
                    void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * Backward pass: the gradients of a loss L with respect to every input of
+ * ssd_fwd, given dL/dy and dL/d final_state.  The pages name this pass (the
+ * Mamba context-parallel backward of "揭秘MindSpeed-LLM多潜在注意力（MLA）与Mamba
+ * 上下文并行实现原理", §三.2) without writing it out; it is the derivative of
+ * the map defined above:
+ *   G_t = C_t^T dy_t + exp(-d_{t+1}) G_{t+1}   (G = dL/dH; G_T adds d_final)
+ *   dx_t = d_t B_t G_t,   dB_t = d_t G_t x_t^T,   dC_t = H_t dy_t,
+ *   dd_t = < G_t, -exp(-d_t) H_{t-1} + B_t^T x_t >,
+ *   d_raw gradient dd_t * sigmoid(d_raw_t + d_init), d_init gradient its sum,
+ *   init_state gradient exp(-d_0) G_0,
+ * with dB and dC summed over the heads of each group.  It runs in the same
+ * chunked form as ssd_fwd (states entering every chunk, then per-chunk
+ * gradients), all in the processing order given by reverse.
+ *
+ * Built for headdim <= 64 and d_state 16, 32, 64 or 128 (bf16) or 16, 32
+ * (float32); other sizes return SSD_ERR_UNSUPPORTED.
+ *
+ * Arguments as ssd_fwd, plus:
+ *   y           the forward output of these inputs (as ssd_fwd wrote it),
+ *               strided like ssd_fwd's y
+ *   dy          dL/dy, dtype, the same layout rules as y (its own strides)
+ *   d_final     dL/d final_state [S, H, N, P] float32, or NULL for zeros
+ *   dx          output [b, L, H, P] dtype, contiguous
+ *   dd_raw      output [b, L, H] dtype
+ *   dB, dC      output [b, L, G, N] dtype
+ *   dinit_state output [S, H, N, P] float32 (the gradient at the given
+ *               init_state, or at zeros when it is NULL), or NULL to skip
+ *   dd_init     output: one float32 on the device, or NULL to skip
+ *   workspace   at least ssd_bwd_workspace_bytes(dims) bytes, 256-byte
+ *               aligned (every call overwrites what it reads; no zero-fill
+ *               needed); calls that overlap in time need separate workspaces
+ * x, B, C, y, dy, dx, dB and dC must be 16-byte aligned; strides are in
+ * elements, multiples of 16 bytes, at most 2^24.  Outputs for tokens outside
+ * every cu_seqlens segment are not written.  Returns SSD_OK once the work
+ * is queued on the stream.
+ */
+size_t ssd_bwd_workspace_bytes(const ssd_dims* dims);
+
+int ssd_bwd(const ssd_dims* dims,
+            const void* x, const void* d_raw, float d_init,
+            const void* B, const void* C,
+            const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+            const void* y, int64_t y_token_stride, int64_t y_head_stride,
+            const void* dy, int64_t dy_token_stride, int64_t dy_head_stride,
+            const float* d_final,
+            void* dx, void* dd_raw, void* dB, void* dC,
+            float* dinit_state, float* dd_init,
+            void* workspace, size_t workspace_bytes,
+            void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);

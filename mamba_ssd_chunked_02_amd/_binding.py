@@ -94,6 +94,22 @@ def library() -> ctypes.CDLL:
         lib.ssd_fwd_stages.argtypes = [ctypes.c_uint32] + fwd_args
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_plan.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(SsdPlanInfo)]
+        lib.ssd_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_bwd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims)]
+        lib.ssd_bwd.restype = ctypes.c_int
+        lib.ssd_bwd.argtypes = [
+            ctypes.POINTER(SsdDims),
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.c_void_p,
+        ]
         _lib = lib
     return _lib
 
@@ -252,3 +268,100 @@ def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,
     _, fr = ssd_fwd(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, True,
                     y=y[..., P:], final_state=final_state, workspace=workspace)
     return y, ((ff, fr) if final_state else None)
+
+
+def ssd_bwd_workspace_bytes(dims: SsdDims) -> int:
+    return int(library().ssd_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def _strided_like_x(t, name, shape, dtype, dev):
+    if tuple(t.shape) != shape or t.dtype != dtype or t.device != dev:
+        raise ValueError(f"{name} must match x in shape, dtype and device")
+    b, L = shape[0], shape[1]
+    if t.stride(3) != 1 or (b > 1 and t.stride(0) != L * t.stride(1)):
+        raise ValueError(f"{name} needs a contiguous last dim and batch stride L*token stride")
+
+
+class PreparedBwd:
+    """Marshalled arguments of one ssd_bwd call (tensors kept alive)."""
+
+    def __init__(self, dims, args, keep, grads, workspace):
+        self.dims = dims
+        self.args = args
+        self._keep = keep
+        self.grads = grads
+        self.workspace = workspace
+
+    def run(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.grads["dx"].device).cuda_stream
+        rc = library().ssd_bwd(ctypes.byref(self.dims), *self.args, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise SsdError(rc, "ssd_bwd")
+        return self.grads
+
+
+def prepare_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size=CHUNK, init_state=None,
+                cu_seqlens=None, reverse=False, d_final=None, workspace=None) -> PreparedBwd:
+    """Check and marshal the arguments of ``ssd_bwd``; allocate the
+    gradients (dict: dx, dd_raw, dB, dC, dinit_state, dd_init) and the
+    workspace when not given."""
+    if x.dim() != 4 or d_raw.dim() != 3 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] expected")
+    b, L, H, P = x.shape
+    dev = x.device
+    for name, t in (("d_raw", d_raw), ("B", B), ("C", C)):
+        if t.device != dev or t.dtype != x.dtype:
+            raise ValueError(f"{name} must be on {dev} with dtype {x.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if tuple(d_raw.shape) != (b, L, H) or tuple(B.shape[:2]) != (b, L) or B.shape != C.shape:
+        raise ValueError("shape mismatch between x, d_raw, B and C")
+    _strided_like_x(y, "y", (b, L, H, P), x.dtype, dev)
+    _strided_like_x(dy, "dy", (b, L, H, P), x.dtype, dev)
+    G, N = B.shape[2], B.shape[3]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on the same device")
+        cu_seqlens = cu_seqlens.contiguous()
+    S = (cu_seqlens.numel() - 1) if cu_seqlens is not None else b
+    for name, t in (("init_state", init_state), ("d_final", d_final)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (S, H, N, P)
+                              or t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [{S},{H},{N},{P}] on {dev}")
+    grads = {
+        "dx": torch.empty_like(x),
+        "dd_raw": torch.empty_like(d_raw),
+        "dB": torch.empty_like(B),
+        "dC": torch.empty_like(C),
+        "dinit_state": torch.empty((S, H, N, P), dtype=torch.float32, device=dev),
+        "dd_init": torch.empty((1,), dtype=torch.float32, device=dev),
+    }
+    dims = dims_for(x, B, chunk_size, cu_seqlens)
+    need = ssd_bwd_workspace_bytes(dims)  # 0 for unsupported sizes: ssd_bwd reports why
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (_ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
+            _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0,
+            _ptr(y), y.stride(1), y.stride(2), _ptr(dy), dy.stride(1), dy.stride(2),
+            _ptr(d_final),
+            _ptr(grads["dx"]), _ptr(grads["dd_raw"]), _ptr(grads["dB"]), _ptr(grads["dC"]),
+            _ptr(grads["dinit_state"]), _ptr(grads["dd_init"]),
+            _ptr(workspace), workspace.numel())
+    keep = (x, d_raw, B, C, y, dy, init_state, cu_seqlens, d_final)
+    return PreparedBwd(dims, args, keep, grads, workspace)
+
+
+def ssd_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size=CHUNK, init_state=None,
+            cu_seqlens=None, reverse=False, d_final=None, workspace=None) -> dict:
+    """Gradients of the SSD scan on the GPU: given the forward inputs, the
+    forward output ``y`` and dL/dy (``dy``, same layout rules as y) and
+    optionally dL/d final_state (``d_final``), returns a dict with dx,
+    dd_raw, dB, dC (input dtype), dinit_state [S,H,N,P] and dd_init [1]
+    (fp32).  Launches on torch's current stream."""
+    call = prepare_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size, init_state, cu_seqlens,
+                       reverse, d_final, workspace)
+    with torch.cuda.device(x.device):
+        return call.run()

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssd.so")
-SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_hw_kernels.hip"]
+SOURCES = ["ssd_api.hip", "ssd_kernels.hip", "ssd_hw_kernels.hip", "ssd_bwd_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 instructions are kept out of the device code (hipcc still

@@ -187,6 +187,74 @@ int make_plan(const ssd_dims* d, Plan* pl) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Backward plan.  Every chunk is its own span, so the two state passes
+// leave the state entering every chunk (forward direction) and the gradient
+// of the state leaving every chunk (walking the chunks backwards) in the
+// workspace; the gradient kernel then treats the chunks independently.  Its
+// workgroups take hs heads of one B/C group; hs is the largest divisor of
+// the group's heads that still gives >= 512 workgroups (SSD_BWD_HEADS
+// overrides it), and the head subsets' dB / dC partials are added after it.
+struct BPlan {
+    int64_t nchunk = 0;    // chunk slots
+    int32_t cps = 0;       // chunks per sequence (batch mode)
+    int32_t nsub = 1, hs = 1;
+    size_t off_cu = 0, off_spoff = 0, off_table = 0;
+    size_t off_sa = 0, off_da = 0, off_sb = 0, off_db = 0;
+    size_t off_pb = 0, off_pc = 0, off_pi = 0, total = 0;
+};
+
+int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
+    Plan pl;
+    const int st = make_plan(d, &pl);  // the forward's size checks
+    if (st != SSD_OK) return st;
+    if (d->headdim > kPGroup || !ssd::bwd_supported(d->dtype, d->d_state)) return SSD_ERR_UNSUPPORTED;
+    const int64_t T = (int64_t)d->batch * d->seqlen;
+    bp->cps = (int32_t)ceil_div(d->seqlen, kChunk);
+    bp->nchunk = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq : (int64_t)d->batch * bp->cps;
+    const int32_t hpg = d->nheads / d->ngroups;
+    int32_t hs = 1;
+    for (int32_t v = hpg; v >= 1; --v) {
+        if (hpg % v == 0 && bp->nchunk * d->ngroups * (hpg / v) >= 512) {
+            hs = v;
+            break;
+        }
+    }
+    if (const char* e = getenv("SSD_BWD_HEADS")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= hpg && hpg % v == 0) hs = v;
+    }
+    bp->hs = hs;
+    bp->nsub = hpg / hs;
+    const size_t esz = d->dtype == SSD_BF16 ? 2 : 4;
+    const size_t states = (size_t)bp->nchunk * d->nheads * d->headdim * d->d_state * esz;
+    const size_t part = (size_t)bp->nsub * T * d->ngroups * d->d_state * sizeof(float);
+    size_t off = align_up(ssd::kSyncHeader * sizeof(uint32_t));
+    if (d->nseq > 0) {
+        bp->off_cu = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        bp->off_spoff = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        bp->off_table = off;
+        off = align_up(off + (size_t)bp->nchunk * sizeof(int4));
+    }
+    bp->off_sa = off;
+    off = align_up(off + states);
+    bp->off_da = off;
+    off = align_up(off + (size_t)bp->nchunk * d->nheads * sizeof(float));
+    bp->off_sb = off;
+    off = align_up(off + states);
+    bp->off_db = off;
+    off = align_up(off + (size_t)bp->nchunk * d->nheads * sizeof(float));
+    bp->off_pb = off;
+    off = align_up(off + part);
+    bp->off_pc = off;
+    off = align_up(off + part);
+    bp->off_pi = off;
+    off = align_up(off + (size_t)bp->nchunk * d->ngroups * bp->nsub * sizeof(float));
+    bp->total = off;
+    return SSD_OK;
+}
+
 // SSD_CHECK=1: copy cu_seqlens to the host (synchronizes the stream) and
 // check 0 = cu[0] <= cu[1] <= ... <= cu[nseq] = L.
 int check_cu(const int32_t* cu, int32_t nseq, int64_t T, hipStream_t s) {
@@ -305,6 +373,8 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.L = d.seqlen;
     p.ys_t = y_token_stride;
     p.ys_h = y_head_stride;
+    p.xs_t = (int64_t)d.nheads * d.headdim;
+    p.xs_h = d.headdim;
     p.nspan = pl.nspan;
     p.batch = d.batch;
     p.H = d.nheads;
@@ -350,6 +420,153 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     return SSD_OK;
+}
+
+size_t ssd_bwd_workspace_bytes(const ssd_dims* dims) {
+    BPlan bp;
+    if (make_bwd_plan(dims, &bp) != SSD_OK) return 0;
+    return bp.total;
+}
+
+int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init, const void* B,
+            const void* C, const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+            const void* y, int64_t y_token_stride, int64_t y_head_stride, const void* dy,
+            int64_t dy_token_stride, int64_t dy_head_stride, const float* d_final, void* dx,
+            void* dd_raw, void* dB, void* dC, float* dinit_state, float* dd_init, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    BPlan bp;
+    const int st = make_bwd_plan(dims, &bp);
+    if (st != SSD_OK) return st;
+    const ssd_dims& d = *dims;
+    const int64_t T = (int64_t)d.batch * d.seqlen;
+    if (T > 0 && (!x || !d_raw || !B || !C || !y || !dy || !dx || !dd_raw || !dB || !dC))
+        return SSD_ERR_NULL_ARG;
+    if (d.nseq > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
+    if (d.nseq == 0 && cu_seqlens) return SSD_ERR_SHAPE;
+    if (reverse != 0 && reverse != 1) return SSD_ERR_SHAPE;
+    const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
+    const int64_t per_unit = 16 / esz;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(dy) ||
+        !aligned16(dx) || !aligned16(dB) || !aligned16(dC))
+        return SSD_ERR_ALIGN;
+    if (((uintptr_t)d_raw % esz) || ((uintptr_t)dd_raw % esz)) return SSD_ERR_ALIGN;
+    for (int64_t v : {y_token_stride, y_head_stride, dy_token_stride, dy_head_stride}) {
+        if (v % per_unit != 0) return SSD_ERR_ALIGN;
+        if (v < 0 || v > ((int64_t)1 << 24)) return SSD_ERR_SHAPE;
+    }
+    if (((uintptr_t)init_state & 3u) || ((uintptr_t)d_final & 3u) || ((uintptr_t)dinit_state & 3u) ||
+        ((uintptr_t)dd_init & 3u))
+        return SSD_ERR_ALIGN;
+    if (!workspace || workspace_bytes < bp.total) return SSD_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % kAlign) return SSD_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    if (d.nseq > 0) {
+        const char* chk = getenv("SSD_CHECK");
+        if (chk && chk[0] == '1') {
+            const int c = check_cu(cu_seqlens, d.nseq, T, s);
+            if (c != SSD_OK) return c;
+        }
+    }
+    char* ws = (char*)workspace;
+    hipError_t e = hipSuccess;
+
+    // state entering every chunk: the forward's span kernels, one chunk per span
+    ssd::KParams pa;
+    memset(&pa, 0, sizeof(pa));
+    pa.x = x;
+    pa.d_raw = d_raw;
+    pa.B = B;
+    pa.C = C;
+    pa.init = init_state;
+    pa.states = ws + bp.off_sa;
+    pa.decay = (float*)(ws + bp.off_da);
+    pa.L = d.seqlen;
+    pa.xs_t = (int64_t)d.nheads * d.headdim;
+    pa.xs_h = d.headdim;
+    pa.nspan = bp.nchunk;
+    pa.batch = d.batch;
+    pa.H = d.nheads;
+    pa.P = d.headdim;
+    pa.G = d.ngroups;
+    pa.N = d.d_state;
+    pa.nseq = d.nseq;
+    pa.K = 1;
+    pa.sps = d.nseq > 0 ? 0 : bp.cps;
+    pa.npg = 1;
+    pa.hg_state = pa.hg_scan = 1;
+    pa.reverse = reverse;
+    pa.sync = (uint32_t*)ws;
+    pa.d_init = d_init;
+    if (d.nseq > 0) {
+        pa.cu = (const int32_t*)(ws + bp.off_cu);
+        pa.span_off = (const int32_t*)(ws + bp.off_spoff);
+        pa.table = (const int4*)(ws + bp.off_table);
+        e = ssd::launch_span_table(cu_seqlens, d.nseq, T, 1, bp.nchunk, (int32_t*)(ws + bp.off_cu),
+                                   (int32_t*)(ws + bp.off_spoff), (int4*)(ws + bp.off_table), s);
+        if (e != hipSuccess) return SSD_ERR_HIP;
+    }
+    e = ssd::launch_span_state(pa, d.dtype, d.d_state, s);
+    if (e == hipSuccess) e = ssd::launch_state_pass(pa, d.dtype, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+
+    // gradient of the state leaving every chunk: the same kernels on (C, dy)
+    // with weights e^{cs_s}, walked from the last chunk back from d_final;
+    // what is left after the first chunk is the initial state's gradient
+    ssd::KParams pg = pa;
+    pg.x = dy;
+    pg.xs_t = dy_token_stride;
+    pg.xs_h = dy_head_stride;
+    pg.B = C;
+    pg.init = d_final;
+    pg.final_state = dinit_state;
+    pg.states = ws + bp.off_sb;
+    pg.decay = (float*)(ws + bp.off_db);
+    pg.wmode = 1;
+    pg.pass_desc = 1;
+    e = ssd::launch_span_state(pg, d.dtype, d.d_state, s);
+    if (e == hipSuccess) e = ssd::launch_state_pass(pg, d.dtype, s);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+
+    ssd::BParams q;
+    memset(&q, 0, sizeof(q));
+    q.x = x;
+    q.d_raw = d_raw;
+    q.B = B;
+    q.C = C;
+    q.y = y;
+    q.dy = dy;
+    q.hprev = ws + bp.off_sa;
+    q.gout = ws + bp.off_sb;
+    q.dx = dx;
+    q.dd_raw = dd_raw;
+    q.dB_part = (float*)(ws + bp.off_pb);
+    q.dC_part = (float*)(ws + bp.off_pc);
+    q.ddi_part = (float*)(ws + bp.off_pi);
+    q.cu = pa.cu;
+    q.table = pa.table;
+    q.L = d.seqlen;
+    q.ntok = T;
+    q.xs_t = (int64_t)d.nheads * d.headdim;
+    q.xs_h = d.headdim;
+    q.ys_t = y_token_stride;
+    q.ys_h = y_head_stride;
+    q.gs_t = dy_token_stride;
+    q.gs_h = dy_head_stride;
+    q.nchunk = bp.nchunk;
+    q.batch = d.batch;
+    q.H = d.nheads;
+    q.P = d.headdim;
+    q.G = d.ngroups;
+    q.N = d.d_state;
+    q.nseq = d.nseq;
+    q.cps = bp.cps;
+    q.nsub = bp.nsub;
+    q.hs = bp.hs;
+    q.reverse = reverse;
+    q.d_init = d_init;
+    e = ssd::launch_bwd_chunk(q, d.dtype, s);
+    if (e == hipSuccess) e = ssd::launch_bwd_reduce(q, d.dtype, dB, dC, dd_init, s);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,582 @@
+// Backward pass of the SSD scan on gfx950: the per-chunk gradient kernel and
+// the reductions after it.
+//
+// The forward map ("Mamba-2架构与LaCT并行计算技术解析", §1.1) per sequence and
+// head is H_t = e^{-d_t} H_{t-1} + d_t B_t^T X_t, y_t = C_t H_t.  Its chunked
+// form ("长序列 Mamba 多卡训练，算力和显存怎么同时省", §一) is differentiated chunk
+// by chunk.  Inside a chunk (cs_t = within-chunk cumulative -d, in processing
+// order, L[t][s] = e^{cs_t - cs_s} for s <= t), with Hprev the state entering
+// the chunk and Gout the gradient of the state leaving it (both formed by the
+// state kernels of the forward pass, the second one walking the chunks
+// backwards from dL/d final_state):
+//
+//   dX_s = d_s [ sum_{t>=s} (C_t.B_s) L[t][s] dy_t + e^{cs_last-cs_s} B_s Gout ]
+//   dB_s = d_s [ sum_{t>=s} (dy_t.X_s) L[t][s] C_t + e^{cs_last-cs_s} Gout X_s ]
+//   dC_t = sum_{s<=t} (dy_t.X_s) L[t][s] d_s B_s + e^{cs_t} Hprev dy_t
+//   dw_s = (dX_s / d_s) . X_s                     (gradient of the input weight)
+//   da_t = <Gout, Hend> + sum_{j>=t} (dy_j.y_j - d_j dw_j)   (log-decay gradient)
+//   <Gout, Hend> = e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last-cs_s} d_s (B_s Gout).X_s
+//   d d_raw_t = (dw_t - da_t) sigmoid(d_raw_t + d_init)
+//
+// The da identity follows from <G_t, H_t> = dy_t.y_t + <G_{t+1}, e^{-d_{t+1}} H_t>
+// and keeps every sum inside one chunk.  dB and dC are summed over the heads
+// of a group: a workgroup takes a subset of those heads and accumulates in
+// registers; the subsets' fp32 partials are added by bwd_reduce.
+#include "ssd_device.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kTiles = 10;  // causal 16x16 blocks (t-block >= s-block) of a chunk
+// index of block (tb, sb), tb >= sb
+__device__ __forceinline__ constexpr int tix(int tb, int sb) { return tb * (tb + 1) / 2 + sb; }
+__device__ __forceinline__ void tile_of(int ti, int& tb, int& sb) {
+    tb = ti >= 6 ? 3 : (ti >= 3 ? 2 : (ti >= 1 ? 1 : 0));
+    sb = ti - tb * (tb + 1) / 2;
+}
+
+// Per-chunk factors of one head (cs in log2 units, c_k = cs at the last token
+// of 16-token block k-1, c_0 = 0).  For t in block tb > sb, s in block sb:
+//   L[t][s] = fb_t * fm(tb, sb) * fa0_s,  fb_t = 2^{cs_t - c_tb} (0 for t past
+//   the chunk's end), fm = 2^{c_tb - c_{sb+1}}, fa0_s = 2^{c_{sb+1} - cs_s}.
+struct __attribute__((aligned(16))) BDecay {
+    float cs2[kChunk];
+    float dt[kChunk];   // d_t (0 past the end)
+    float fe[kChunk];   // 2^{cs_t}
+    float wl[kChunk];   // 2^{cs_last - cs_s}
+    float fa0[kChunk];
+    float fb[kChunk];
+    float sg[kChunk];   // sigmoid(d_raw_t + d_init) = softplus'
+    float fm[8];
+};
+
+template <typename T>
+__device__ __forceinline__ void bwd_factors(BDecay& D, uint32_t raw, float d_init, int clen,
+                                            int lane) {
+    const float draw = __uint_as_float(sizeof(T) == 2 ? raw << 16 : raw);
+    const float z = draw + d_init;
+    const float dt = lane < clen ? softplus(z) : 0.f;
+    const float v = wave_prefix_sum(-dt * kLog2e);
+    const float c1 = lane_value(v, 15), c2 = lane_value(v, 31);
+    const float c3 = lane_value(v, 47), c4 = lane_value(v, 63);
+    const int sb = lane >> 4;
+    const float cbeg = sb == 0 ? 0.f : (sb == 1 ? c1 : (sb == 2 ? c2 : c3));
+    const float cend = sb == 0 ? c1 : (sb == 1 ? c2 : (sb == 2 ? c3 : c4));
+    D.cs2[lane] = v;
+    D.dt[lane] = dt;
+    D.fe[lane] = fexp2(v);
+    D.wl[lane] = fexp2(c4 - v);
+    D.fa0[lane] = fexp2(cend - v);
+    D.fb[lane] = lane < clen ? fexp2(v - cbeg) : 0.f;
+    const float ez = fexp2(-fabsf(z) * kLog2e);  // e^{-|z|}
+    D.sg[lane] = (z >= 0.f ? 1.f : ez) / (1.f + ez);
+    if (lane < 6) {
+        // (tb, sb) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): 2^{c_tb - c_{sb+1}}
+        const float ct = lane == 0 ? c1 : (lane < 3 ? c2 : c3);
+        const float cs = (lane == 0 || lane == 1 || lane == 3) ? c1 : ((lane == 2 || lane == 4) ? c2 : c3);
+        D.fm[lane] = fexp2(ct - cs);
+    }
+}
+
+template <typename T, int N>
+struct BCfg {
+    static constexpr int NB = N / 16;            // 16-row blocks of the state
+    static constexpr int KN = (N + 31) / 32;     // K=32 steps over the state dim
+    static constexpr int EPU = 16 / sizeof(T);   // elements per 16-byte unit
+    static constexpr int W = 16 / EPU;           // 16-byte units per block row
+    static constexpr int BI = NB * W;            // load instructions of a B / C tile
+};
+
+// LDS of one backward workgroup.  Tiles are column-blocked (boff); the two
+// states keep their HBM order (state_off), which is MFMA result order.
+template <typename T, int N>
+struct __attribute__((aligned(16))) BSmem {
+    using X4 = typename Vec<T>::x4;
+    T bs[kChunk * N];          // B of the chunk (group)
+    T cs[kChunk * N];          // C
+    T xs[kChunk * kPGroup];    // X of the head (blocks past the headdim stay 0)
+    T gy[kChunk * kPGroup];    // dL/dy
+    T ys[kChunk * kPGroup];    // y
+    T gr[kPGroup * N];         // Gout (entries past P*N stay 0)
+    T hr[kPGroup * N];         // Hprev
+    f32x4 cb[kTiles][64];      // C B^T blocks (t rows, s columns), result order
+    X4 f1[kTiles][64];         // (C B^T) o L, rows t: B operand of dy^T A1
+    X4 f2[kTiles][64];         // (dy X^T) o L, times d_s, rows t: dB
+    X4 f3[kTiles][64];         // the same product transposed (rows s): dC
+    BDecay dec;
+    float red[3][kWaves][kChunk];  // per-wave partial dw, zx, dy.y
+    float gh[kWaves];              // per-wave partial <Gout, Hprev>
+    __attribute__((aligned(16))) uint32_t dr[kChunk];
+};
+
+// An operand fragment with every element times f, rounded back to T.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x8 scale8(const typename Vec<T>::x8& v, float f) {
+    typename Vec<T>::x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = cvt<T>((float)v[j] * f);
+    return r;
+}
+
+// A-operand fragment of a state kept in state order (rows n = 16nb + l16 of
+// the lane's group, K = headdim p in {32kp + 4g + k, 32kp + 16 + 4g + k}).
+// bf16: the transposing read gathers, for lane i of a 16-lane group, entry
+// (n = 16nb + i, p0 + k) into slot k when lane j of the group addresses the
+// 4-entry run (n-quad 4nb + j%4, p = p0 + j/4).
+template <int NB>
+__device__ __forceinline__ bf16x8 state_frag_t(const bf16* st, int nb, int kp, int g, int lane) {
+    const int j = lane & 15;
+    bf16x4 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int pp = 32 * kp + 16 * half + 4 * g + (j >> 2);
+        const int off = (((pp >> 4) * NB + nb) * 64 + 16 * (j & 3) + (pp & 15)) * 4;
+        h[half] = ldtr(st + off);
+    }
+    return cat<bf16x8, bf16x4>(h[0], h[1]);
+}
+template <int NB>
+__device__ __forceinline__ f32x8 state_frag_t(const float* st, int nb, int kp, int g, int lane) {
+    const int n = 16 * nb + (lane & 15);
+    f32x8 v;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int pp = 32 * kp + 16 * half + 4 * g + k;
+            v[4 * half + k] = st[(((pp >> 4) * NB + nb) * 64 + 16 * ((n & 15) >> 2) + (pp & 15)) * 4 + (n & 3)];
+        }
+    return v;
+}
+
+// Masked block (TB, SB) in (t rows, s columns) orientation: lane (s, g) holds
+// t = 16TB + 4g + i.  ws = d_s or 1.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x4 mask_ts(const f32x4& acc, const BDecay& D, int TB,
+                                                      int SB, int lane, int clen, bool with_d) {
+    typename Vec<T>::x4 v;
+    const int s = 16 * SB + (lane & 15), t0 = 16 * TB + 4 * (lane >> 4);
+    const float ds = with_d ? D.dt[s] : 1.f;
+    if (TB > SB) {
+        const float f = D.fm[TB * (TB - 1) / 2 + SB] * D.fa0[s] * ds;
+        const f32x4 fb = *(const f32x4*)&D.fb[t0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(acc[i] * (fb[i] * f));
+    } else {
+        const float css = D.cs2[s];
+        const f32x4 cst = *(const f32x4*)&D.cs2[t0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = s <= t0 + i && t0 + i < clen;
+            v[i] = cvt<T>(ok ? acc[i] * fexp2(cst[i] - css) * ds : 0.f);
+        }
+    }
+    return v;
+}
+// Masked block (TB, SB) in (s rows, t columns) orientation: lane (t, g) holds
+// s = 16SB + 4g + i, times d_s.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x4 mask_st(const f32x4& acc, const BDecay& D, int TB,
+                                                      int SB, int lane, int clen) {
+    typename Vec<T>::x4 v;
+    const int t = 16 * TB + (lane & 15), s0 = 16 * SB + 4 * (lane >> 4);
+    const f32x4 dts = *(const f32x4*)&D.dt[s0];
+    if (TB > SB) {
+        const float f = D.fm[TB * (TB - 1) / 2 + SB] * D.fb[t];
+        const f32x4 fa = *(const f32x4*)&D.fa0[s0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(acc[i] * (fa[i] * dts[i] * f));
+    } else {
+        const float cst = D.cs2[t];
+        const f32x4 css = *(const f32x4*)&D.cs2[s0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = s0 + i <= t && t < clen;
+            v[i] = cvt<T>(ok ? acc[i] * fexp2(cst - css[i]) * dts[i] : 0.f);
+        }
+    }
+    return v;
+}
+
+__device__ __forceinline__ float xor_add(float v, int m) {
+    return v + __shfl_xor(v, m, 64);
+}
+
+// One workgroup: one chunk, one B/C group, one subset of that group's heads
+// (headdim <= 64).  Four waves; per head:
+//   load X, dy, y, Gout, Hprev and d_raw; one wave forms the decay factors;
+//   every wave masks its share of the 30 causal blocks (C B^T, formed once per
+//   workgroup, and dy X^T in both orientations); wave w then forms dX for
+//   headdim columns 16w..16w+15, and accumulates dB for tokens 16w.. (s
+//   block w) and dC for tokens 16w.. (t block w) -- the causal work of the
+//   two is complementary, so the waves stay balanced; wave 0 turns the
+//   per-token sums into d d_raw.
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
+    using Cf = BCfg<T, N>;
+    using X8 = typename Vec<T>::x8;
+    using X4 = typename Vec<T>::x4;
+    constexpr int NB = Cf::NB, KN = Cf::KN, W = Cf::W, BI = Cf::BI, EPU = Cf::EPU;
+    __shared__ BSmem<T, N> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int l16 = lane & 15, g = lane >> 4;
+
+    const int64_t item = blockIdx.x;
+    const int sub = (int)(item % p.nsub);
+    const int grp = (int)((item / p.nsub) % p.G);
+    const int64_t chunk = item / p.nsub / p.G;
+    int64_t start = 0, len = 0, kc = 0;
+    bool valid = true;
+    if (p.nseq) {
+        const int4 e = p.table[chunk];
+        if (e.x < 0) {
+            valid = false;
+        } else {
+            start = p.cu[e.x];
+            len = (int64_t)p.cu[e.x + 1] - start;
+            kc = e.y;
+        }
+    } else {
+        const int64_t seq = chunk / p.cps;
+        kc = chunk - seq * p.cps;
+        start = seq * p.L;
+        len = p.L;
+    }
+    const int64_t cj0 = kc * kChunk;
+    if (!valid || cj0 >= len) {
+        if (tid == 0) p.ddi_part[item] = 0.f;
+        return;
+    }
+    const int clen = (int)imin(kChunk, len - cj0);
+    const int dir = p.reverse ? -1 : 1;
+    const int64_t tb0 = start + (p.reverse ? len - 1 - cj0 : cj0);
+    auto tok = [&](int r) -> int64_t { return tb0 + dir * r; };
+    const int hpg = p.H / p.G;
+    const int h0 = grp * hpg + sub * p.hs;
+    const int h1 = min(h0 + p.hs, (grp + 1) * hpg);
+    const int P = p.P, npb = P / 16, PN = P * N;
+    const int GN = p.G * N;
+
+    // zero what no load fills: X / dy / y blocks past the headdim, state
+    // entries past P*N (they meet the zero columns of X and dy in K)
+    for (int i = npb * kChunk * 16 + tid; i < kChunk * kPGroup; i += kThreads) {
+        sm.xs[i] = cvt<T>(0.f);
+        sm.gy[i] = cvt<T>(0.f);
+        sm.ys[i] = cvt<T>(0.f);
+    }
+    for (int i = PN + tid; i < kPGroup * N; i += kThreads) {
+        sm.gr[i] = cvt<T>(0.f);
+        sm.hr[i] = cvt<T>(0.f);
+    }
+    issue_tile<(BI + kWaves - 1) / kWaves, kWaves, BI>(sm.bs, (const T*)p.B + tb0 * GN + grp * N,
+                                                     dir * GN, wave, clen, N, lane);
+    issue_tile<(BI + kWaves - 1) / kWaves, kWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
+                                                     dir * GN, wave, clen, N, lane);
+    vm_wait<0>();
+    block_sync();
+    // C B^T once for the group: block (tb, sb) = rows t, columns s
+    for (int ti = wave; ti < kTiles; ti += kWaves) {
+        int TB, SB;
+        tile_of(ti, TB, SB);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk)
+            acc = mma(tile_frag<N>(sm.cs, 16 * TB + l16, kk, g), tile_frag<N>(sm.bs, 16 * SB + l16, kk, g), acc);
+        sm.cb[ti][lane] = acc;
+    }
+
+    f32x4 dBt[NB], dCt[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dBt[nb] = dCt[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ddi = 0.f;
+    const BDecay& D = sm.dec;
+    const X4 z4 = {};
+
+    for (int h = h0; h < h1; ++h) {
+        // this head's tiles (wave w loads headdim block w) and states
+        if (wave < npb) {
+            issue_tile<W, 1, 4 * W>(sm.xs, (const T*)p.x + tb0 * p.xs_t + h * p.xs_h, dir * (int)p.xs_t,
+                                    wave * W, clen, P, lane);
+            issue_tile<W, 1, 4 * W>(sm.gy, (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h, dir * (int)p.gs_t,
+                                    wave * W, clen, P, lane);
+            issue_tile<W, 1, 4 * W>(sm.ys, (const T*)p.y + tb0 * p.ys_t + h * p.ys_h, dir * (int)p.ys_t,
+                                    wave * W, clen, P, lane);
+        }
+        const int64_t hb = (chunk * p.H + h) * (int64_t)PN;
+        for (int i = wave; i * 64 * EPU < PN; i += kWaves) {
+            const int o = (i * 64 + lane) * EPU;
+            if (o < PN) {
+                __builtin_amdgcn_global_load_lds((const void*)((const T*)p.gout + hb + o),
+                                                 (__attribute__((address_space(3))) void*)(sm.gr + i * 64 * EPU),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)((const T*)p.hprev + hb + o),
+                                                 (__attribute__((address_space(3))) void*)(sm.hr + i * 64 * EPU),
+                                                 16, 0, 0);
+            }
+        }
+        if (wave == 0) {
+            const void* src = (const void*)((const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h);
+            auto* lds = (__attribute__((address_space(3))) void*)sm.dr;
+            if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
+            else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+        }
+        vm_wait<0>();
+        block_sync();
+        if (wave == 0) bwd_factors<T>(sm.dec, sm.dr[lane], p.d_init, clen, lane);
+        block_sync();
+
+        // masked blocks: A1 = (C B^T) o L; A2 = (dy X^T) o L d_s in both orientations
+        for (int ti = wave; ti < kTiles; ti += kWaves) {
+            int TB, SB;
+            tile_of(ti, TB, SB);
+            sm.f1[ti][lane] = mask_ts<T>(sm.cb[ti][lane], D, TB, SB, lane, clen, false);
+            f32x4 m = {0.f, 0.f, 0.f, 0.f}, mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                const X8 yt = tile_frag<kPGroup>(sm.gy, 16 * TB + l16, kp, g);
+                const X8 xs = tile_frag<kPGroup>(sm.xs, 16 * SB + l16, kp, g);
+                m = mma(yt, xs, m);
+                mt = mma(xs, yt, mt);
+            }
+            sm.f2[ti][lane] = mask_ts<T>(m, D, TB, SB, lane, clen, true);
+            sm.f3[ti][lane] = mask_st<T>(mt, D, TB, SB, lane, clen);
+        }
+        block_sync();
+
+        // dX for headdim block `wave` (transposed: lane (s, g) holds p = 4g + i)
+        float gh = 0.f;
+        if (wave < npb) {
+            X8 gyf[2], gf[KN];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) gyf[j] = tok_frag(sm.gy, 32 * j + 4 * g, 32 * j + 16 + 4 * g, wave, lane);
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk) {
+                const X4 lo = ld4(sm.gr + ((wave * NB + 2 * kk) * 64 + lane) * 4);
+                const X4 hi = 2 * kk + 1 < NB ? ld4(sm.gr + ((wave * NB + 2 * kk + 1) * 64 + lane) * 4) : z4;
+                gf[kk] = cat<X8, X4>(lo, hi);
+            }
+#pragma unroll
+            for (int SB = 0; SB < 4; ++SB) {
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accG = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (2 * j + 1 < SB) continue;
+                    const X4 lo = 2 * j >= SB ? sm.f1[tix(2 * j, SB)][lane] : z4;
+                    const X4 hi = sm.f1[tix(2 * j + 1, SB)][lane];
+                    accA = mma(gyf[j], cat<X8, X4>(lo, hi), accA);
+                }
+#pragma unroll
+                for (int kk = 0; kk < KN; ++kk) accG = mma(gf[kk], tile_frag<N>(sm.bs, 16 * SB + l16, kk, g), accG);
+                const int s = 16 * SB + l16;
+                const float wl = D.wl[s], ds = D.dt[s];
+                f32x4 raw;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) raw[i] = accA[i] + wl * accG[i];
+                if (s < clen) store4((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * wave + 4 * g, ds * raw);
+                const X4 xv = tld4(sm.xs, s, wave, 4 * g);
+                const X4 gv = tld4(sm.gy, s, wave, 4 * g);
+                const X4 yv = tld4(sm.ys, s, wave, 4 * g);
+                float dw = 0.f, zx = 0.f, yy = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dw += raw[i] * (float)xv[i];
+                    zx += accG[i] * (float)xv[i];
+                    yy += (float)gv[i] * (float)yv[i];
+                }
+                dw = xor_add(xor_add(dw, 16), 32);
+                zx = xor_add(xor_add(zx, 16), 32);
+                yy = xor_add(xor_add(yy, 16), 32);
+                if (g == 0) {
+                    sm.red[0][wave][s] = dw;
+                    sm.red[1][wave][s] = zx;
+                    sm.red[2][wave][s] = yy;
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const X4 gv = ld4(sm.gr + ((wave * NB + nb) * 64 + lane) * 4);
+                const X4 hv = ld4(sm.hr + ((wave * NB + nb) * 64 + lane) * 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gh += (float)gv[i] * (float)hv[i];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) sm.red[k][wave][lane] = 0.f;
+        }
+        gh = wave_prefix_sum(gh);
+        if (lane == 63) sm.gh[wave] = gh;
+
+        // dB for tokens s in block `wave`: d_s sum_t A2[t][s] C_t + w_s Gout X_s
+        {
+            const int SB = wave;
+            X8 a2[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const X4 lo = 2 * j >= SB ? sm.f2[tix(2 * j, SB)][lane] : z4;
+                const X4 hi = 2 * j + 1 >= SB ? sm.f2[tix(2 * j + 1, SB)][lane] : z4;
+                a2[j] = cat<X8, X4>(lo, hi);
+            }
+            const int s = 16 * SB + l16;
+            const float ws = D.wl[s] * D.dt[s];
+            X8 xw[2];
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) xw[kp] = scale8<T>(tile_frag<kPGroup>(sm.xs, s, kp, g), ws);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (2 * j + 1 >= SB)
+                        dBt[nb] = mma(tok_frag(sm.cs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a2[j], dBt[nb]);
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+                    dBt[nb] = mma(state_frag_t<NB>(sm.gr, nb, kp, g, lane), xw[kp], dBt[nb]);
+            }
+        }
+        // dC for tokens t in block `wave`: sum_s A2[t][s] d_s B_s + e^{cs_t} Hprev dy_t
+        {
+            const int TB = wave;
+            X8 a3[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const X4 lo = 2 * j <= TB ? sm.f3[tix(TB, 2 * j)][lane] : z4;
+                const X4 hi = 2 * j + 1 <= TB ? sm.f3[tix(TB, 2 * j + 1)][lane] : z4;
+                a3[j] = cat<X8, X4>(lo, hi);
+            }
+            const int t = 16 * TB + l16;
+            const float fe = D.fe[t];
+            X8 gw[2];
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) gw[kp] = scale8<T>(tile_frag<kPGroup>(sm.gy, t, kp, g), fe);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (2 * j <= TB)
+                        dCt[nb] = mma(tok_frag(sm.bs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a3[j], dCt[nb]);
+#pragma unroll
+                for (int kp = 0; kp < 2; ++kp)
+                    dCt[nb] = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], dCt[nb]);
+            }
+        }
+        block_sync();
+
+        // per-token sums -> d d_raw (wave 0, lane = token)
+        if (wave == 0) {
+            const int s = lane;
+            float dw = 0.f, zx = 0.f, yy = 0.f, ghs = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                dw += sm.red[0][w][s];
+                zx += sm.red[1][w][s];
+                yy += sm.red[2][w][s];
+                ghs += sm.gh[w];
+            }
+            const bool in = s < clen;
+            const float ds = D.dt[s];
+            // <Gout, Hend>: e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last - cs_s} d_s zx_s
+            const float ez = lane_value(wave_prefix_sum(in ? D.wl[s] * ds * zx : 0.f), 63);
+            const float E = D.fe[kChunk - 1] * ghs + ez;
+            const float r = in ? yy - ds * dw : 0.f;
+            const float incl = wave_prefix_sum(r);
+            const float da = E + lane_value(incl, 63) - incl + r;  // E + sum_{j >= s} r_j
+            const float gr = (dw - da) * D.sg[s];
+            if (in) ((T*)p.dd_raw)[tok(s) * p.H + h] = cvt<T>(gr);
+            ddi += in ? gr : 0.f;
+        }
+        block_sync();  // every read of this head's LDS is done
+    }
+
+    // this subset's partial dB (s block `wave`) and dC (t block `wave`)
+    {
+        const int s = 16 * wave + l16;
+        if (s < clen) {
+            const int64_t o = ((int64_t)sub * p.ntok + tok(s)) * GN + grp * N + 4 * g;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                *(f32x4*)(p.dB_part + o + 16 * nb) = dBt[nb];
+                *(f32x4*)(p.dC_part + o + 16 * nb) = dCt[nb];
+            }
+        }
+    }
+    if (wave == 0) {
+        ddi = lane_value(wave_prefix_sum(ddi), 63);
+        if (lane == 0) p.ddi_part[item] = ddi;
+    }
+}
+
+// dB / dC: the sum of the head subsets' fp32 partials, in the input type.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* part, int nsub, int64_t n4,
+                                                         T* out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 acc = *(const f32x4*)(part + 4 * i);
+    for (int k = 1; k < nsub; ++k) acc += *(const f32x4*)(part + 4 * (k * n4 + i));
+    store4(out + 4 * i, acc);
+}
+
+// d d_init: the sum of every workgroup's partial, in a fixed order.
+__global__ __launch_bounds__(256) void bwd_dinit_kernel(const float* part, int64_t n, float* out) {
+    __shared__ float sh[256];
+    float acc = 0.f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) acc += part[i];
+    sh[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = sh[0];
+}
+
+template <typename T, int N>
+hipError_t launch_bwd_t(const BParams& p, hipStream_t s) {
+    const int64_t grid = p.nchunk * p.G * p.nsub;
+    if (grid > 0)
+        hipLaunchKernelGGL((bwd_chunk_kernel<T, N>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int dtype, int N) {
+    return dtype == 1 ? (N == 16 || N == 32 || N == 64 || N == 128) : (N == 16 || N == 32);
+}
+
+hipError_t launch_bwd_chunk(const BParams& p, int dtype, hipStream_t s) {
+    if (dtype == 1) {
+        switch (p.N) {
+            case 16: return launch_bwd_t<bf16, 16>(p, s);
+            case 32: return launch_bwd_t<bf16, 32>(p, s);
+            case 64: return launch_bwd_t<bf16, 64>(p, s);
+            case 128: return launch_bwd_t<bf16, 128>(p, s);
+        }
+    } else {
+        switch (p.N) {
+            case 16: return launch_bwd_t<float, 16>(p, s);
+            case 32: return launch_bwd_t<float, 32>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, float* dd_init,
+                             hipStream_t s) {
+    const int64_t n4 = p.ntok * p.G * p.N / 4;
+    if (n4 > 0) {
+        const dim3 grid((unsigned)((n4 + 255) / 256));
+        if (dtype == 1) {
+            hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, grid, dim3(256), 0, s, p.dB_part, p.nsub, n4, (bf16*)dB);
+            hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, grid, dim3(256), 0, s, p.dC_part, p.nsub, n4, (bf16*)dC);
+        } else {
+            hipLaunchKernelGGL(bwd_reduce_kernel<float>, grid, dim3(256), 0, s, p.dB_part, p.nsub, n4, (float*)dB);
+            hipLaunchKernelGGL(bwd_reduce_kernel<float>, grid, dim3(256), 0, s, p.dC_part, p.nsub, n4, (float*)dC);
+        }
+    }
+    if (dd_init)
+        hipLaunchKernelGGL(bwd_dinit_kernel, dim3(1), dim3(256), 0, s, p.ddi_part,
+                           p.nchunk * p.G * p.nsub, dd_init);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

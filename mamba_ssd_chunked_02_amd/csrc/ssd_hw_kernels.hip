@@ -266,9 +266,9 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1)
     const int nvb = max(0, min(NPB, (pgw - 16 * blk0) / 16));  // blocks inside the headdim
 
     const int dir = p.reverse ? -1 : 1;
-    const int HP = p.H * p.P, GN = p.G * N;
+    const int XS = (int)p.xs_t, GN = p.G * N;
     const int grp = (int)((int64_t)h0 * p.G / p.H);
-    const bf16* const xg = (const bf16*)p.x + (int64_t)h * p.P + pcol0;
+    const bf16* const xg = (const bf16*)p.x + (int64_t)h * p.xs_h + pcol0;
     const bf16* const bg = (const bf16*)p.B + (int64_t)grp * N;
     const bf16* const cg = (const bf16*)p.C + (int64_t)grp * N;
     const bf16* const dg = (const bf16*)p.d_raw + h;
@@ -278,17 +278,17 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1)
     const int64_t rem0 = len - cj0;
     auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(c * dstep); };
     auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
-    const bf16* const xc0 = xg + tb0 * HP;
+    const bf16* const xc0 = xg + tb0 * XS;
     const bf16* const bc0 = bg + tb0 * GN;
     const bf16* const cc0 = cg + tb0 * GN;
-    const int64_t xcs = (int64_t)dstep * HP, bcs = (int64_t)dstep * GN;
+    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * GN;
 
     // Chunk c's tiles: the waves of a head split its X tile, all waves split
     // B and C.  d_raw of a chunk: the head's first wave, one token per lane.
     auto issue_tiles = [&](int c, bf16* __restrict__ xdst, bf16* __restrict__ bdst,
                            bf16* __restrict__ cdst) {
         const int cl = clen_of(c);
-        issue_tile<Cf::XIW, 1, Cf::XI>(xdst, xc0 + c * xcs, dir * HP, wc * Cf::XIW, cl, pgw, lane);
+        issue_tile<Cf::XIW, 1, Cf::XI>(xdst, xc0 + c * xcs, dir * XS, wc * Cf::XIW, cl, pgw, lane);
         issue_tile<Cf::BIW, NW, Cf::BI>(bdst, bc0 + c * bcs, dir * GN, wave, cl, N, lane);
         if constexpr (SCAN)
             issue_tile<Cf::BIW, NW, Cf::BI>(cdst, cc0 + c * bcs, dir * GN, wave, cl, N, lane);

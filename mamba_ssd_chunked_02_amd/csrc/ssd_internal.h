@@ -31,6 +31,8 @@ struct KParams {
     const int4* table;      // [nspan] {seq, chunk0, nchunks, 0} (varlen)
     int64_t L;              // tokens per batch row
     int64_t ys_t, ys_h;     // y strides (elements)
+    int64_t xs_t, xs_h;     // x strides (elements): token, head (H*P and P
+                            // for a contiguous x)
     int64_t nspan;          // span slots (grid extent)
     int32_t batch, H, P, G, N;
     int32_t nseq;           // 0 = batch mode
@@ -49,8 +51,46 @@ struct KParams {
     uint32_t* sync;         // workspace header; for fuse_pass 2 followed by one
                             // 64-bit ticket/epoch word per chain and one flag
                             // per workgroup
+    int32_t wmode;          // state-update weights of span_state: 0 the
+                            // forward's e^{cs_last - cs_s} d_s, 1 e^{cs_s}
+                            // (the backward's output-gradient state)
+    int32_t pass_desc;      // state_pass walks each sequence's spans from
+                            // its last to its first
     float d_init;
 };
+
+// Backward pass (ssd_bwd_kernels.hip): one workgroup per (chunk, B/C
+// group, subset of hs heads of the group); headdim <= 64.
+struct BParams {
+    const void* x;          // [b, L, H, P] (strides xs_t, xs_h; dx shares them)
+    const void* d_raw;      // [b, L, H]
+    const void* B;          // [b, L, G, N]
+    const void* C;
+    const void* y;          // forward output (strides ys_t, ys_h)
+    const void* dy;         // dL/dy (strides gs_t, gs_h)
+    const void* hprev;      // [nchunk][H][P*N] state entering each chunk
+    const void* gout;       // [nchunk][H][P*N] dL/d(state leaving each chunk)
+    void* dx;               // [b, L, H, P]
+    void* dd_raw;           // [b, L, H]
+    float* dB_part;         // [nsub][ntok][G][N] per head subset
+    float* dC_part;
+    float* ddi_part;        // [nchunk * G * nsub] per workgroup
+    const int32_t* cu;      // sanitized cu_seqlens (varlen) or null
+    const int4* table;      // [nchunk] {seq, chunk, 1, 0} (varlen)
+    int64_t L, ntok;        // tokens per batch row, b * L
+    int64_t xs_t, xs_h, ys_t, ys_h, gs_t, gs_h;
+    int64_t nchunk;         // chunk slots (grid extent / G / nsub)
+    int32_t batch, H, P, G, N;
+    int32_t nseq;
+    int32_t cps;            // chunks per sequence (batch mode)
+    int32_t nsub, hs;       // head subsets per group, heads per subset
+    int32_t reverse;
+    float d_init;
+};
+bool bwd_supported(int dtype, int N);
+hipError_t launch_bwd_chunk(const BParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, float* dd_init,
+                             hipStream_t s);
 
 // Most spans per sequence for which span_scan forms the incoming states
 // itself (each workgroup folds all earlier spans of its sequence).

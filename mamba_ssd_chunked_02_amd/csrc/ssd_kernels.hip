@@ -286,12 +286,12 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
 
     // Token of row r of chunk c: tok0(c) + dir * r.
     const int dir = p.reverse ? -1 : 1;
-    const int HP = p.H * p.P, GN = p.G * N;
+    const int XS = (int)p.xs_t, GN = p.G * N;
     const int grp = (int)((int64_t)h0 * p.G / p.H);
     // Every wave computes, with a valid head even in a quad without one or
     // past the headdim; only active waves store what they computed.
     const int hc = live ? h : h0;
-    const T* const xg = (const T*)p.x + (int64_t)hc * p.P + pcol0;
+    const T* const xg = (const T*)p.x + (int64_t)hc * p.xs_h + pcol0;
     const T* const bg = (const T*)p.B + (int64_t)grp * N;
     const T* const cg = (const T*)p.C + (int64_t)grp * N;
     const T* const dg = (const T*)p.d_raw + hc;
@@ -304,15 +304,15 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
     auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(c * dstep); };
     auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
     // chunk c's row-0 pointers: base at chunk 0 plus c chunk steps
-    const T* const xc0 = xg + tb0 * HP;
+    const T* const xc0 = xg + tb0 * XS;
     const T* const bc0 = bg + tb0 * GN;
     const T* const cc0 = cg + tb0 * GN;
-    const int64_t xcs = (int64_t)dstep * HP, bcs = (int64_t)dstep * GN;
+    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * GN;
     // Chunk c's X tile (wave w4 loads its own 16-column block) and this
     // wave's share of the B tile.
     auto issue_xb = [&](int c, T* __restrict__ xdst, T* __restrict__ bdst) {
         const int cl = clen_of(c);
-        issue_tile<W, 1, XI>(xdst, xc0 + c * xcs, dir * HP, w4 * W, cl, pgw, lane);
+        issue_tile<W, 1, XI>(xdst, xc0 + c * xcs, dir * XS, w4 * W, cl, pgw, lane);
         issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + c * bcs, dir * GN, wave, cl, N,
                                                         lane);
     };
@@ -558,7 +558,13 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
 #pragma unroll
                     for (int kk = 0; kk < kChunk / 32; ++kk) {
                         const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
-                        const f32x8 ws = ld8(&D.w[s0]);
+                        f32x8 ws = ld8(p.wmode ? &D.fe[s0] : &D.w[s0]);
+                        // e^{cs_s} does not vanish past a partial chunk's end
+                        // (d_s does): rows there hold row 0 again
+                        if (p.wmode && cl < kChunk) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) ws[j] = s0 + j < cl ? ws[j] : 0.f;
+                        }
                         const X8 xv = tok_frag(xt, s0, s0 + 4, w4, lane);
                         X8 b, bt[NB];
 #pragma unroll
@@ -701,23 +707,27 @@ __global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
         for (int j = 0; j < V; ++j) run[j] = p.init[hb + idx[j]];
     }
     TSV* st = (TSV*)p.states;
-    for (int64_t k = s0; k < s1; k += U) {
+    // span number k of the walk: s0 + k, or s1 - 1 - k walking backwards
+    const int64_t ns = s1 - s0;
+    auto span_at = [&](int64_t k) { return p.pass_desc ? s1 - 1 - k : s0 + k; };
+    for (int64_t k = 0; k < ns; k += U) {
         TSV v[U];
         float d[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k + u < s1) {
-                v[u] = st[((k + u) * p.H + h) * EV + ev];
-                d[u] = p.decay[(k + u) * p.H + h];
+            if (k + u < ns) {
+                const int64_t sp = span_at(k + u);
+                v[u] = st[(sp * p.H + h) * EV + ev];
+                d[u] = p.decay[sp * p.H + h];
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k + u < s1) {
+            if (k + u < ns) {
                 TSV o;
 #pragma unroll
                 for (int j = 0; j < V; ++j) o[j] = (TS)run[j];
-                st[((k + u) * p.H + h) * EV + ev] = o;
+                st[(span_at(k + u) * p.H + h) * EV + ev] = o;
 #pragma unroll
                 for (int j = 0; j < V; ++j) run[j] = d[u] * run[j] + (float)v[u][j];
             }

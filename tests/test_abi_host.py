@@ -181,3 +181,67 @@ def test_plan_head_wave_kernels(m, monkeypatch):
     assert small.head_wave == 1 and small.fused_pass == 0
     monkeypatch.setenv("SSD_KERNEL", "span")
     assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16)).head_wave == 0
+
+
+def call_bwd(m, dims, **kw):
+    H, P = (dims.nheads, dims.headdim) if dims else (2, 16)
+    args = dict(x=FAKE, d_raw=FAKE, d_init=-4.6, B=FAKE, C=FAKE, init=None, cu=None, reverse=0,
+                y=FAKE, yst=H * P, ysh=P, dy=FAKE, gst=H * P, gsh=P, dfin=None, dx=FAKE,
+                ddr=FAKE, dB=FAKE, dC=FAKE, dinit=None, ddi=None, ws=FAKE, wsb=1 << 40,
+                stream=None)
+    args.update(kw)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)
+    a = args
+    return m.library().ssd_bwd(
+        ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)(), vp(a["x"]), vp(a["d_raw"]),
+        a["d_init"], vp(a["B"]), vp(a["C"]), vp(a["init"]), vp(a["cu"]), a["reverse"], vp(a["y"]),
+        a["yst"], a["ysh"], vp(a["dy"]), a["gst"], a["gsh"], vp(a["dfin"]), vp(a["dx"]),
+        vp(a["ddr"]), vp(a["dB"]), vp(a["dC"]), vp(a["dinit"]), vp(a["ddi"]), vp(a["ws"]),
+        a["wsb"], vp(a["stream"]))
+
+
+def test_bwd_workspace_bytes(m):
+    """Two per-chunk state sets dominate: 2 * chunks * H * P * N * e, plus the
+    head subsets' fp32 dB / dC partials; unsupported sizes give 0."""
+    d = m.make_dims(2, 2048, 24, 64, 128)
+    ws = m.ssd_bwd_workspace_bytes(d)
+    states = 2 * 64 * 24 * 64 * 128 * 2
+    assert states < ws < states + 2 * 24 * 4096 * 128 * 4 + (1 << 20)
+    assert ws % 256 == 0
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 128, 64)) == 0      # headdim > 64
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 64, 256)) == 0      # d_state 256
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 64, dtype=0)) == 0
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 32, dtype=0)) > 0
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 0, 2, 16, 16)) > 0         # empty input
+
+
+def test_bwd_head_subsets(m, monkeypatch):
+    """The gradient kernel's head subsets: the largest divisor of the group's
+    heads that keeps >= 512 workgroups -- fewer subsets, smaller partials."""
+    few = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))   # 1024 chunks
+    monkeypatch.setenv("SSD_BWD_HEADS", "1")
+    many = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))
+    part = (24 - 1) * 2 * 64 * 1024 * 128 * 4   # 23 more subsets of dB and dC partials
+    assert part <= many - few < part + (1 << 20)
+
+
+@needs_no_gpu
+def test_bwd_rejects_bad_arguments(m):
+    ok = m.make_dims(1, 128, 2, 64, 128)
+    assert call_bwd(m, None) == -1
+    assert call_bwd(m, ok, dy=None) == -1                                  # NULL_ARG
+    assert call_bwd(m, ok, dB=None) == -1
+    assert call_bwd(m, ok, y=None) == -1
+    assert call_bwd(m, m.make_dims(1, 128, 2, 128, 128)) == -5             # headdim > 64
+    assert call_bwd(m, m.make_dims(1, 128, 2, 64, 256)) == -5
+    assert call_bwd(m, m.make_dims(1, 128, 2, 24, 128)) == -2
+    assert call_bwd(m, m.make_dims(1, 128, 2, 64, 128, nseq=2)) == -1      # cu_seqlens missing
+    assert call_bwd(m, ok, cu=FAKE) == -2
+    assert call_bwd(m, ok, reverse=3) == -2
+    assert call_bwd(m, ok, dy=FAKE + 8) == -4                              # ALIGN
+    assert call_bwd(m, ok, dx=FAKE + 4) == -4
+    assert call_bwd(m, ok, gst=64 * 2 + 4) == -4
+    assert call_bwd(m, ok, gst=1 << 25) == -2
+    assert call_bwd(m, ok, ddr=FAKE + 1) == -4
+    assert call_bwd(m, ok, ws=None) == -6                                  # WORKSPACE
+    assert call_bwd(m, ok, wsb=16) == -6

@@ -1,0 +1,143 @@
+"""GPU parity of the backward pass: libssd's ssd_bwd (through its C ABI)
+against the fp64 backward oracle (the adjoint of the recurrence, itself
+pinned by finite differences in test_oracle_bwd_pins.py).
+
+Bound per gradient (max|gpu - ref| / max|ref|): BWD_TOL for bf16 inputs
+(fp32 accumulation; the operands of every product are rounded to bf16,
+states included), 1e-5 for fp32 inputs.  The forward output y the backward
+reads is the GPU's own, as a caller would pass it; dy and d_final are seeded
+Gaussians.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ssd_oracle as F
+from oracle import ssd_oracle_bwd as O
+from ssd_inputs import random_problem
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-5}
+DEV = "cuda:0"
+KEYS = ("dx", "dd_raw", "dB", "dC", "dinit_state")
+
+
+@pytest.fixture(scope="module")
+def ssd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mamba_ssd_chunked_02_amd as m
+    m.library()
+    return m
+
+
+def _dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def bwd_case(ssd, p, reverse=False, with_final=True, seed=0, label=""):
+    dt = p["x"].dtype
+    tol = BWD_TOL[dt]
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    y, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                       init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], reverse=reverse)
+    g = torch.Generator().manual_seed(seed)
+    dy = torch.randn(p["x"].shape, generator=g).to(dt)
+    b, L, H, P = p["x"].shape
+    N = p["B"].shape[3]
+    S = b if p["cu_seqlens"] is None else p["cu_seqlens"].numel() - 1
+    dfin = torch.randn((S, H, N, P), generator=g) if with_final else None
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, _dev(dy),
+                      init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], reverse=reverse,
+                      d_final=_dev(dfin))
+    torch.cuda.synchronize()
+    ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                        init_state=p["init_state"], d_final=dfin, cu_seqlens=p["cu_seqlens"],
+                        reverse=reverse)
+    errs = {k: F.rel_err(got[k].float().cpu(), ref[k]) for k in KEYS}
+    errs["dd_init"] = abs(float(got["dd_init"].cpu()) - ref["dd_init"]) / max(
+        float(np.abs(ref["dd_raw"]).sum()), 1e-30)
+    print(f"{label} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" tol={tol}",
+          flush=True)
+    for k in KEYS:
+        assert torch.isfinite(got[k].float()).all(), k
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    return got, ref
+
+
+SHAPES = [
+    # (batch, seqlen, nheads, headdim, d_state, ngroups)
+    (2, 200, 4, 64, 128, 1),
+    (1, 130, 4, 32, 64, 2),
+    (1, 64, 2, 16, 16, 1),
+    (1, 65, 3, 48, 32, 1),
+    (1, 1, 2, 64, 128, 1),
+]
+
+
+@pytest.mark.parametrize("rev", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_shapes_bf16(ssd, shape, rev):
+    b, L, H, P, N, G = shape
+    p = random_problem(301, b, L, H, P, N, ngroups=G, dtype="bf16", init_scale=0.5, d_init=-2.0)
+    bwd_case(ssd, p, reverse=rev, label=f"bwd {shape} rev={rev}")
+
+
+@pytest.mark.parametrize("N", [16, 32])
+def test_bwd_fp32(ssd, N):
+    p = random_problem(307, 1, 256, 2, 16, N, dtype="f32", init_scale=0.5, d_init=-4.6)
+    bwd_case(ssd, p, label=f"bwd fp32 N={N}")
+    bwd_case(ssd, p, reverse=True, label=f"bwd fp32 N={N} rev")
+
+
+def test_bwd_varlen(ssd):
+    """Packed sequences with an empty one and ragged tails: every state pass
+    restarts at a boundary, the empty sequence hands d_final straight to its
+    initial-state gradient."""
+    p = random_problem(311, 1, 0, 4, 64, 128, dtype="bf16", init_scale=0.5, d_init=-2.0,
+                       lengths=[70, 0, 129, 64, 1])
+    bwd_case(ssd, p, label="bwd varlen")
+    bwd_case(ssd, p, reverse=True, label="bwd varlen rev")
+
+
+def test_bwd_no_state_gradients(ssd):
+    """No initial state and no final-state gradient."""
+    p = random_problem(313, 2, 150, 2, 64, 64, dtype="bf16", d_init=-4.6)
+    bwd_case(ssd, p, with_final=False, label="bwd no-state")
+
+
+def test_bwd_head_subsets(ssd, monkeypatch):
+    """One head per workgroup (24 partials of dB / dC added) and all heads in
+    one workgroup give the same gradients within the bound."""
+    p = random_problem(317, 1, 256, 6, 64, 128, dtype="bf16", init_scale=0.5, d_init=-2.0)
+    for hs in ("1", "6"):
+        monkeypatch.setenv("SSD_BWD_HEADS", hs)
+        bwd_case(ssd, p, label=f"bwd heads/wg={hs}")
+
+
+def test_bwd_layer_shape(ssd):
+    """Layer-shaped problem (24 heads x headdim 64, d_state 128) at 512 tokens."""
+    p = random_problem(331, 1, 512, 24, 64, 128, dtype="bf16", d_init=-4.6)
+    bwd_case(ssd, p, with_final=False, label="bwd layer-shaped")
+
+
+def test_bwd_strided_dy_and_y(ssd):
+    """dy and y as halves of a [b, L, H, 2P] buffer (the bidirectional layout)."""
+    p = random_problem(337, 1, 100, 2, 32, 64, dtype="bf16", init_scale=0.5, d_init=-2.0)
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    b, L, H, P = p["x"].shape
+    ycat = torch.empty((b, L, H, 2 * P), dtype=torch.bfloat16, device=DEV)
+    ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"],
+                y=ycat[..., P:])
+    g = torch.Generator().manual_seed(5)
+    dy = torch.randn((b, L, H, P), generator=g).to(torch.bfloat16)
+    dycat = torch.zeros((b, L, H, 2 * P), dtype=torch.bfloat16)
+    dycat[..., :P] = dy
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], ycat[..., P:],
+                      dycat.to(DEV)[..., :P], init_state=d["init_state"])
+    ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                        init_state=p["init_state"])
+    for k in KEYS:
+        assert F.rel_err(got[k].float().cpu(), ref[k]) <= BWD_TOL[torch.bfloat16], k
