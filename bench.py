@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the SSD chunked-scan forward on one MI355X.
+"""Benchmark of the SSD chunked-scan forward (and backward) on one MI355X.
 
 One step = one full ``ssd_fwd`` (all stages) over the "layer" workload:
 batch 2 x 2048 tokens, 24 heads x headdim 64, d_state 128, bf16 inputs,
@@ -20,6 +20,11 @@ HBM before timing starts.  Prints one JSON line:
   since the counters were taken.
 * cpu_baseline          -- the C fp64 oracle (test infrastructure) timed on
   this host on the same workload, repeated for ~10 s.
+* bwd                   -- outside the timed region: the backward pass
+  (``ssd_bwd``, gradients of every input for a seeded dL/dy and dL/d
+  final_state) on the same workload, W warm-up calls then K calls between
+  two stream synchronizations; null where the backward is not built for
+  the sizes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -134,6 +139,8 @@ def main() -> int:
     ap.add_argument("--workload", default="layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward leg (profiles of the forward kernels alone)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warm-up, run 3 plain device copies of this many MiB "
                          "(reference kernel for scaling rocprofv3 byte counters)")
@@ -266,6 +273,26 @@ def main() -> int:
         "ms_per_step_with_stage_events": round(wall_ev / K * 1e3, 5),
         "cpu_baseline": None,
     }
+    out["bwd"] = None
+    if not args.no_bwd and not w.bidir and m.ssd_bwd_workspace_bytes(calls[0].dims) > 0:
+        y, fin = calls[0].run()
+        g = torch.Generator(device=dev).manual_seed(7)
+        dy = torch.randn(y.shape, generator=g, device=dev).to(y.dtype)
+        dfin = torch.randn(fin.shape, generator=g, device=dev)
+        bcall = m.prepare_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, dy,
+                              init_state=d["init_state"], cu_seqlens=d["cu_seqlens"],
+                              d_final=dfin)
+        for _ in range(args.warmup):
+            bcall.run()
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(K):
+            bcall.run()
+        torch.cuda.synchronize()
+        bwd_ms = (time.perf_counter() - tb) / K * 1e3
+        out["bwd"] = {"ms_per_step": round(bwd_ms, 5),
+                      "value": round(tokens / (bwd_ms * 1e-3) / 1e6, 3), "unit": "Mtokens/s",
+                      "steps": K, "warmup": args.warmup}
     if not args.no_cpu_baseline and host is not None:
         out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_budget)
     print(json.dumps(out), flush=True)

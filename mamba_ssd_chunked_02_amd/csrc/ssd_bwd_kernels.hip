@@ -504,29 +504,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
     }
 }
 
-// dB / dC: the sum of the head subsets' fp32 partials, in the input type.
+// One launch after the gradient kernel: workgroups 0 .. nblk-1 add the head
+// subsets' fp32 partials of dB (first half of the grid) and dC (second
+// half) and store them in the input type; the last workgroup sums every
+// gradient workgroup's d d_init partial in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* part, int nsub, int64_t n4,
-                                                         T* out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;
-    f32x4 acc = *(const f32x4*)(part + 4 * i);
-    for (int k = 1; k < nsub; ++k) acc += *(const f32x4*)(part + 4 * (k * n4 + i));
-    store4(out + 4 * i, acc);
-}
-
-// d d_init: the sum of every workgroup's partial, in a fixed order.
-__global__ __launch_bounds__(256) void bwd_dinit_kernel(const float* part, int64_t n, float* out) {
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* pb, const float* pc,
+                                                         int nsub, int64_t n4, int64_t nblk,
+                                                         T* dB, T* dC, const float* ddi_part,
+                                                         int64_t nddi, float* dd_init) {
+    const int64_t blk = blockIdx.x;
+    if (blk < 2 * nblk) {
+        const bool second = blk >= nblk;
+        const float* part = second ? pc : pb;
+        T* out = second ? dC : dB;
+        const int64_t i = (blk - (second ? nblk : 0)) * 256 + threadIdx.x;
+        if (i >= n4) return;
+        f32x4 acc = *(const f32x4*)(part + 4 * i);
+        for (int k = 1; k < nsub; ++k) acc += *(const f32x4*)(part + 4 * (k * n4 + i));
+        store4(out + 4 * i, acc);
+        return;
+    }
     __shared__ float sh[256];
     float acc = 0.f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) acc += part[i];
+    for (int64_t i = threadIdx.x; i < nddi; i += 256) acc += ddi_part[i];
     sh[threadIdx.x] = acc;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
         if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
         __syncthreads();
     }
-    if (threadIdx.x == 0) *out = sh[0];
+    if (threadIdx.x == 0) *dd_init = sh[0];
 }
 
 template <typename T, int N>
@@ -563,19 +571,16 @@ hipError_t launch_bwd_chunk(const BParams& p, int dtype, hipStream_t s) {
 hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, float* dd_init,
                              hipStream_t s) {
     const int64_t n4 = p.ntok * p.G * p.N / 4;
-    if (n4 > 0) {
-        const dim3 grid((unsigned)((n4 + 255) / 256));
-        if (dtype == 1) {
-            hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, grid, dim3(256), 0, s, p.dB_part, p.nsub, n4, (bf16*)dB);
-            hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, grid, dim3(256), 0, s, p.dC_part, p.nsub, n4, (bf16*)dC);
-        } else {
-            hipLaunchKernelGGL(bwd_reduce_kernel<float>, grid, dim3(256), 0, s, p.dB_part, p.nsub, n4, (float*)dB);
-            hipLaunchKernelGGL(bwd_reduce_kernel<float>, grid, dim3(256), 0, s, p.dC_part, p.nsub, n4, (float*)dC);
-        }
-    }
-    if (dd_init)
-        hipLaunchKernelGGL(bwd_dinit_kernel, dim3(1), dim3(256), 0, s, p.ddi_part,
-                           p.nchunk * p.G * p.nsub, dd_init);
+    const int64_t nblk = (n4 + 255) / 256;
+    const int64_t grid = 2 * nblk + (dd_init ? 1 : 0);
+    if (grid == 0) return hipSuccess;
+    const int64_t nddi = p.nchunk * p.G * p.nsub;
+    if (dtype == 1)
+        hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, s, p.dB_part,
+                           p.dC_part, p.nsub, n4, nblk, (bf16*)dB, (bf16*)dC, p.ddi_part, nddi, dd_init);
+    else
+        hipLaunchKernelGGL(bwd_reduce_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, p.dB_part,
+                           p.dC_part, p.nsub, n4, nblk, (float*)dB, (float*)dC, p.ddi_part, nddi, dd_init);
     return hipGetLastError();
 }
 
