@@ -129,10 +129,11 @@ __device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay&
 // Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
 // per CU, or one 8-wave one; lighter variants get more from their natural
 // register use.  A scan with state rows wider than 256 bytes gets 512.
-enum { kModeState = 0, kModeScan = 1, kModeFused = 2 };
+enum { kModeState = 0, kModeScan = 1, kModeFused = 2, kModeStateGrad = 3 };
+constexpr bool is_state(int mode) { return mode == kModeState || mode == kModeStateGrad; }
 template <typename T, int N, int HG, int MODE>
 constexpr int span_occupancy() {
-    return HG == 1 && !(MODE != kModeState && N * sizeof(T) > 256) ? 2 : 1;
+    return HG == 1 && !(!is_state(MODE) && N * sizeof(T) > 256) ? 2 : 1;
 }
 
 // Accesses coherent across the whole device (agent scope, all XCDs): the
@@ -185,6 +186,9 @@ __device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" :
 // Span workgroups.
 //  kModeState  the span's local state from a zero state, and its decay
 //              product (span_state).
+//  kModeStateGrad  the same with weights e^{cs_s} in place of
+//              e^{cs_last - cs_s} d_s: on (C, dy) the backward pass's
+//              chunk-local output-gradient state.
 //  kModeScan   y from the state entering the span: as state_pass left it,
 //              or (fuse_pass 1) folded here from the span states of the
 //              earlier spans of the sequence, with the last span then also
@@ -205,10 +209,10 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
     constexpr int NB = Cf::NB, KN = Cf::KN, EPU = Cf::EPU;
     constexpr int W = 16 / EPU;               // 16-byte units per block row
     constexpr int XI = 4 * W, BI = NB * W;    // load instructions per X / B / C tile
-    constexpr bool SCANL = MODE != kModeState;  // LDS holds the scan buffers
+    constexpr bool SCANL = !is_state(MODE);  // LDS holds the scan buffers
     __shared__ Smem<T, N, HG, SCANL> sm;
 
-    const int hg = MODE == kModeState ? p.hg_state : p.hg_scan;
+    const int hg = is_state(MODE) ? p.hg_state : p.hg_scan;
     const int ngrp = (p.H + hg - 1) / hg;
     const int64_t nreal = p.nspan * ngrp * p.npg;
     const int tid = threadIdx.x;
@@ -558,12 +562,14 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
 #pragma unroll
                     for (int kk = 0; kk < kChunk / 32; ++kk) {
                         const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
-                        f32x8 ws = ld8(p.wmode ? &D.fe[s0] : &D.w[s0]);
-                        // e^{cs_s} does not vanish past a partial chunk's end
-                        // (d_s does): rows there hold row 0 again
-                        if (p.wmode && cl < kChunk) {
+                        f32x8 ws = ld8(MODE == kModeStateGrad ? &D.fe[s0] : &D.w[s0]);
+                        if constexpr (MODE == kModeStateGrad) {
+                            // e^{cs_s} does not vanish past a partial chunk's
+                            // end (d_s does): rows there hold row 0 again
+                            if (cl < kChunk) {
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) ws[j] = s0 + j < cl ? ws[j] : 0.f;
+                                for (int j = 0; j < 8; ++j) ws[j] = s0 + j < cl ? ws[j] : 0.f;
+                            }
                         }
                         const X8 xv = tok_frag(xt, s0, s0 + 4, w4, lane);
                         X8 b, bt[NB];
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
         }
     };
 
-    if constexpr (MODE == kModeState) {
+    if constexpr (is_state(MODE)) {
         run(std::false_type{});
         if (active) {
 #pragma unroll
@@ -817,8 +823,8 @@ hipError_t launch_span_hg(const KParams& p, int hg, hipStream_t s) {
 // can carry at this d_state.
 template <typename T, int N, int MODE>
 hipError_t launch_span_t(const KParams& p, hipStream_t s) {
-    constexpr int MAXH = MODE != kModeState ? heads_scan(N, sizeof(T)) : heads_state(N, sizeof(T));
-    const int hg = MODE != kModeState ? p.hg_scan : p.hg_state;
+    constexpr int MAXH = !is_state(MODE) ? heads_scan(N, sizeof(T)) : heads_state(N, sizeof(T));
+    const int hg = !is_state(MODE) ? p.hg_scan : p.hg_state;
     if (hg == 1) return launch_span_hg<T, N, 1, MODE>(p, 1, s);
     if (hg == 2 && MAXH >= 2) return launch_span_hg<T, N, (MAXH >= 2 ? 2 : 1), MODE>(p, 2, s);
     return hipErrorInvalidValue;
@@ -885,7 +891,7 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T, int
 }
 
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s) {
-    return launch_span<kModeState>(p, dtype, N, s);
+    return p.wmode ? launch_span<kModeStateGrad>(p, dtype, N, s) : launch_span<kModeState>(p, dtype, N, s);
 }
 
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s) {
