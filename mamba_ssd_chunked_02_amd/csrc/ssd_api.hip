@@ -192,8 +192,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // of the state leaving every chunk (walking the chunks backwards) in the
 // workspace; the gradient kernel then treats the chunks independently.  Its
 // workgroups take hs heads of one B/C group; hs is the largest divisor of
-// the group's heads that still gives >= 512 workgroups (SSD_BWD_HEADS
-// overrides it), and the head subsets' dB / dC partials are added after it.
+// the group's heads that still gives >= 256 workgroups, one per CU (the
+// kernel's LDS allows one; SSD_BWD_HEADS overrides it), and the head
+// subsets' dB / dC partials are added after it.
 struct BPlan {
     int64_t nchunk = 0;    // chunk slots
     int32_t cps = 0;       // chunks per sequence (batch mode)
@@ -214,7 +215,7 @@ int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
     const int32_t hpg = d->nheads / d->ngroups;
     int32_t hs = 1;
     for (int32_t v = hpg; v >= 1; --v) {
-        if (hpg % v == 0 && bp->nchunk * d->ngroups * (hpg / v) >= 512) {
+        if (hpg % v == 0 && bp->nchunk * d->ngroups * (hpg / v) >= 256) {
             hs = v;
             break;
         }
@@ -505,13 +506,11 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
                                    (int32_t*)(ws + bp.off_spoff), (int4*)(ws + bp.off_table), s);
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
-    e = ssd::launch_span_state(pa, d.dtype, d.d_state, s);
-    if (e == hipSuccess) e = ssd::launch_state_pass(pa, d.dtype, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
 
     // gradient of the state leaving every chunk: the same kernels on (C, dy)
     // with weights e^{cs_s}, walked from the last chunk back from d_final;
-    // what is left after the first chunk is the initial state's gradient
+    // what is left after the first chunk is the initial state's gradient.
+    // The two directions are independent: each kernel pair is one launch.
     ssd::KParams pg = pa;
     pg.x = dy;
     pg.xs_t = dy_token_stride;
@@ -523,8 +522,8 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     pg.decay = (float*)(ws + bp.off_db);
     pg.wmode = 1;
     pg.pass_desc = 1;
-    e = ssd::launch_span_state(pg, d.dtype, d.d_state, s);
-    if (e == hipSuccess) e = ssd::launch_state_pass(pg, d.dtype, s);
+    e = ssd::launch_span_state_pair(pa, pg, d.dtype, d.d_state, s);
+    if (e == hipSuccess) e = ssd::launch_state_pass_pair(pa, pg, d.dtype, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
 
     ssd::BParams q;

@@ -35,6 +35,15 @@ __device__ __forceinline__ void tile_of(int ti, int& tb, int& sb) {
     sb = ti - tb * (tb + 1) / 2;
 }
 
+// The two states sit in LDS in their HBM order (state_off: runs of 4 entries,
+// run (pb, nb, g, l) holding n = 16nb + 4g + 0..3 at p = 16pb + l) with the
+// column l of run XORed with 4g.  The transposing reads of state_frag_t then
+// meet 16 distinct 8-byte bank pairs per 16-lane group (4 n-quads x 4
+// columns), the 8-byte reads of whole result fragments stay a permutation of
+// one 128-byte row per group, and a 16-byte register chunk (two runs, l and
+// l + 1 with l even) stays contiguous.  Element offset of run r:
+__device__ __forceinline__ int srun(int r) { return ((r & ~15) | ((r & 15) ^ (4 * ((r >> 4) & 3)))) * 4; }
+
 // Per-chunk factors of one head (cs in log2 units, c_k = cs at the last token
 // of 16-token block k-1, c_0 = 0).  For t in block tb > sb, s in block sb:
 //   L[t][s] = fb_t * fm(tb, sb) * fa0_s,  fb_t = 2^{cs_t - c_tb} (0 for t past
@@ -88,7 +97,8 @@ struct BCfg {
 };
 
 // LDS of one backward workgroup.  Tiles are column-blocked (boff); the two
-// states keep their HBM order (state_off), which is MFMA result order.
+// states keep their HBM order (state_off, MFMA result order) up to the run
+// swizzle of srun.
 template <typename T, int N>
 struct __attribute__((aligned(16))) BSmem {
     using X4 = typename Vec<T>::x4;
@@ -105,7 +115,7 @@ struct __attribute__((aligned(16))) BSmem {
     X4 f3[kTiles][64];         // the same product transposed (rows s): dC
     BDecay dec;
     float red[3][kWaves][kChunk];  // per-wave partial dw, zx, dy.y
-    float gh[kWaves];              // per-wave partial <Gout, Hprev>
+    float gh[8];                   // per-wave partial <Gout, Hprev>
     __attribute__((aligned(16))) uint32_t dr[kChunk];
 };
 
@@ -130,8 +140,7 @@ __device__ __forceinline__ bf16x8 state_frag_t(const bf16* st, int nb, int kp, i
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int pp = 32 * kp + 16 * half + 4 * g + (j >> 2);
-        const int off = (((pp >> 4) * NB + nb) * 64 + 16 * (j & 3) + (pp & 15)) * 4;
-        h[half] = ldtr(st + off);
+        h[half] = ldtr(st + srun(((pp >> 4) * NB + nb) * 64 + 16 * (j & 3) + (pp & 15)));
     }
     return cat<bf16x8, bf16x4>(h[0], h[1]);
 }
@@ -144,7 +153,7 @@ __device__ __forceinline__ f32x8 state_frag_t(const float* st, int nb, int kp, i
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int pp = 32 * kp + 16 * half + 4 * g + k;
-            v[4 * half + k] = st[(((pp >> 4) * NB + nb) * 64 + 16 * ((n & 15) >> 2) + (pp & 15)) * 4 + (n & 3)];
+            v[4 * half + k] = st[srun(((pp >> 4) * NB + nb) * 64 + 16 * ((n & 15) >> 2) + (pp & 15)) + (n & 3)];
         }
     return v;
 }
@@ -203,23 +212,29 @@ __device__ __forceinline__ float xor_add(float v, int m) {
 }
 
 // One workgroup: one chunk, one B/C group, one subset of that group's heads
-// (headdim <= 64).  Four waves; per head:
-//   load X, dy, y, Gout, Hprev and d_raw; one wave forms the decay factors;
-//   every wave masks its share of the 30 causal blocks (C B^T, formed once per
-//   workgroup, and dy X^T in both orientations); wave w then forms dX for
-//   headdim columns 16w..16w+15, and accumulates dB for tokens 16w.. (s
-//   block w) and dC for tokens 16w.. (t block w) -- the causal work of the
-//   two is complementary, so the waves stay balanced; wave 0 turns the
-//   per-token sums into d d_raw.
+// (headdim <= 64), eight waves in two quads (q = wave / 4, w4 = wave % 4).
+// Per head:
+//   its X, dy, y, states and d_raw arrive (prefetched during the previous
+//   head); one wave forms the decay factors; the waves mask the 30 causal
+//   blocks (C B^T, formed once per workgroup, and dy X^T in both
+//   orientations); wave (q, w4) forms dX for headdim block w4 and token
+//   blocks 2q, 2q+1, and accumulates dB for token block w4 (s) and dC for
+//   token block w4 (t) over half q of the state rows -- the causal work of dB
+//   and dC per token block is complementary, so the waves stay balanced;
+//   wave 0 turns the per-token sums into d d_raw.
+constexpr int kBWaves = 8;
+constexpr int kBThreads = 64 * kBWaves;
 template <typename T, int N>
-__global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
+__global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     using Cf = BCfg<T, N>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
     constexpr int NB = Cf::NB, KN = Cf::KN, W = Cf::W, BI = Cf::BI, EPU = Cf::EPU;
+    constexpr int NBH = (NB + 1) / 2;  // state-row blocks per quad
     __shared__ BSmem<T, N> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l16 = lane & 15, g = lane >> 4;
+    const int q = wave >> 2, w4 = wave & 3;
 
     const int64_t item = blockIdx.x;
     const int sub = (int)(item % p.nsub);
@@ -259,23 +274,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
 
     // zero what no load fills: X / dy / y blocks past the headdim, state
     // entries past P*N (they meet the zero columns of X and dy in K)
-    for (int i = npb * kChunk * 16 + tid; i < kChunk * kPGroup; i += kThreads) {
+    for (int i = npb * kChunk * 16 + tid; i < kChunk * kPGroup; i += kBThreads) {
         sm.xs[i] = cvt<T>(0.f);
         sm.gy[i] = cvt<T>(0.f);
         sm.ys[i] = cvt<T>(0.f);
     }
-    for (int i = PN + tid; i < kPGroup * N; i += kThreads) {
+    for (int i = PN + tid; i < kPGroup * N; i += kBThreads) {
         sm.gr[i] = cvt<T>(0.f);
         sm.hr[i] = cvt<T>(0.f);
     }
-    issue_tile<(BI + kWaves - 1) / kWaves, kWaves, BI>(sm.bs, (const T*)p.B + tb0 * GN + grp * N,
-                                                     dir * GN, wave, clen, N, lane);
-    issue_tile<(BI + kWaves - 1) / kWaves, kWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
-                                                     dir * GN, wave, clen, N, lane);
+    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.bs, (const T*)p.B + tb0 * GN + grp * N,
+                                                         dir * GN, wave, clen, N, lane);
+    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
+                                                         dir * GN, wave, clen, N, lane);
     vm_wait<0>();
     block_sync();
     // C B^T once for the group: block (tb, sb) = rows t, columns s
-    for (int ti = wave; ti < kTiles; ti += kWaves) {
+    for (int ti = wave; ti < kTiles; ti += kBWaves) {
         int TB, SB;
         tile_of(ti, TB, SB);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -285,48 +300,93 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
         sm.cb[ti][lane] = acc;
     }
 
-    f32x4 dBt[NB], dCt[NB];
+    f32x4 dBt[NBH], dCt[NBH];  // state rows 16 (q NBH + i) + 4g + (0..3)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) dBt[nb] = dCt[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NBH; ++i) dBt[i] = dCt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ddi = 0.f;
     const BDecay& D = sm.dec;
     const X4 z4 = {};
 
-    for (int h = h0; h < h1; ++h) {
-        // this head's tiles (wave w loads headdim block w) and states
-        if (wave < npb) {
-            issue_tile<W, 1, 4 * W>(sm.xs, (const T*)p.x + tb0 * p.xs_t + h * p.xs_h, dir * (int)p.xs_t,
-                                    wave * W, clen, P, lane);
-            issue_tile<W, 1, 4 * W>(sm.gy, (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h, dir * (int)p.gs_t,
-                                    wave * W, clen, P, lane);
-            issue_tile<W, 1, 4 * W>(sm.ys, (const T*)p.y + tb0 * p.ys_t + h * p.ys_h, dir * (int)p.ys_t,
-                                    wave * W, clen, P, lane);
+    // A head's X, dy and y tiles, its two states and its d_raw go through
+    // registers: the next head's loads are issued as soon as this head's
+    // data is in LDS, and written to LDS after this head's last LDS read, so
+    // their latency hides behind this head's products.  Tile rows follow the
+    // direct-to-LDS mapping of issue_tile (instruction i fills 1 KB, lane l
+    // its 16 bytes); wave w carries instructions w, w + 8, ... of each tile.
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int TI = (4 * W + kBWaves - 1) / kBWaves;  // tile units per lane
+    constexpr int SI = (kPGroup * N * (int)sizeof(T) / 1024 + kBWaves - 1) / kBWaves;  // state units
+    u32x4 rx[TI], ry[TI], ryy[TI], rg[SI], rh[SI];
+    uint32_t rdr = 0;
+    auto tile_off = [&](int i, int64_t rstride) -> int64_t {
+        const int j = (i % W) * 64 + lane;
+        const int pr = j / W, pu = j % W;
+        const int b3 = (pr >> 3) & 1;
+        const int r = pr ^ (b3 << 2);
+        const int col = (i / W) * 16 + (pu ^ b3) * EPU;
+        return clen == kChunk || r < clen ? r * rstride + col : col;
+    };
+    auto fetch = [&](int h) {
+        const T* xr = (const T*)p.x + tb0 * p.xs_t + h * p.xs_h;
+        const T* gr = (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h;
+        const T* yr = (const T*)p.y + tb0 * p.ys_t + h * p.ys_h;
+#pragma unroll
+        for (int k = 0; k < TI; ++k) {
+            const int i = wave + kBWaves * k;
+            if (i < 4 * W && i / W < npb) {
+                rx[k] = *(const u32x4*)(xr + tile_off(i, dir * p.xs_t));
+                ry[k] = *(const u32x4*)(gr + tile_off(i, dir * p.gs_t));
+                ryy[k] = *(const u32x4*)(yr + tile_off(i, dir * p.ys_t));
+            }
         }
         const int64_t hb = (chunk * p.H + h) * (int64_t)PN;
-        for (int i = wave; i * 64 * EPU < PN; i += kWaves) {
-            const int o = (i * 64 + lane) * EPU;
+#pragma unroll
+        for (int k = 0; k < SI; ++k) {
+            const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
             if (o < PN) {
-                __builtin_amdgcn_global_load_lds((const void*)((const T*)p.gout + hb + o),
-                                                 (__attribute__((address_space(3))) void*)(sm.gr + i * 64 * EPU),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)((const T*)p.hprev + hb + o),
-                                                 (__attribute__((address_space(3))) void*)(sm.hr + i * 64 * EPU),
-                                                 16, 0, 0);
+                rg[k] = *(const u32x4*)((const T*)p.gout + hb + o);
+                rh[k] = *(const u32x4*)((const T*)p.hprev + hb + o);
             }
         }
         if (wave == 0) {
-            const void* src = (const void*)((const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h);
-            auto* lds = (__attribute__((address_space(3))) void*)sm.dr;
-            if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
-            else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+            const T* src = (const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h;
+            if constexpr (sizeof(T) == 2) rdr = *(const uint16_t*)src;
+            else rdr = *(const uint32_t*)src;
         }
-        vm_wait<0>();
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int k = 0; k < TI; ++k) {
+            const int i = wave + kBWaves * k;
+            if (i < 4 * W && i / W < npb) {
+                const int o = (i * 64 + lane) * EPU;
+                *(u32x4*)(sm.xs + o) = rx[k];
+                *(u32x4*)(sm.gy + o) = ry[k];
+                *(u32x4*)(sm.ys + o) = ryy[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < SI; ++k) {
+            const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
+            if (o < PN) {
+                const int so = srun(o / 4);  // the chunk's first run (EPU/4 runs, adjacent)
+                *(u32x4*)(sm.gr + so) = rg[k];
+                *(u32x4*)(sm.hr + so) = rh[k];
+            }
+        }
+        if (wave == 0) sm.dr[lane] = rdr;
+    };
+    fetch(h0);
+
+    for (int h = h0; h < h1; ++h) {
+        stash();
         block_sync();
+        if (h + 1 < h1) fetch(h + 1);
         if (wave == 0) bwd_factors<T>(sm.dec, sm.dr[lane], p.d_init, clen, lane);
         block_sync();
 
         // masked blocks: A1 = (C B^T) o L; A2 = (dy X^T) o L d_s in both orientations
-        for (int ti = wave; ti < kTiles; ti += kWaves) {
+        for (int ti = wave; ti < kTiles; ti += kBWaves) {
             int TB, SB;
             tile_of(ti, TB, SB);
             sm.f1[ti][lane] = mask_ts<T>(sm.cb[ti][lane], D, TB, SB, lane, clen, false);
@@ -343,27 +403,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
         }
         block_sync();
 
-        // dX for headdim block `wave` (transposed: lane (s, g) holds p = 4g + i)
+        // dX for headdim block w4, token blocks 2q and 2q + 1 (transposed:
+        // lane (s, g) holds p = 16 w4 + 4g + i)
         float gh = 0.f;
-        if (wave < npb) {
-            X8 gyf[2], gf[KN];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) gyf[j] = tok_frag(sm.gy, 32 * j + 4 * g, 32 * j + 16 + 4 * g, wave, lane);
+        if (w4 < npb) {
+            X8 gf[KN];
 #pragma unroll
             for (int kk = 0; kk < KN; ++kk) {
-                const X4 lo = ld4(sm.gr + ((wave * NB + 2 * kk) * 64 + lane) * 4);
-                const X4 hi = 2 * kk + 1 < NB ? ld4(sm.gr + ((wave * NB + 2 * kk + 1) * 64 + lane) * 4) : z4;
+                const X4 lo = ld4(sm.gr + srun((w4 * NB + 2 * kk) * 64 + lane));
+                const X4 hi = 2 * kk + 1 < NB ? ld4(sm.gr + srun((w4 * NB + 2 * kk + 1) * 64 + lane)) : z4;
                 gf[kk] = cat<X8, X4>(lo, hi);
             }
 #pragma unroll
-            for (int SB = 0; SB < 4; ++SB) {
+            for (int sh = 0; sh < 2; ++sh) {
+                const int SB = 2 * q + sh;
                 f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accG = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    if (2 * j + 1 < SB) continue;
+                    if (2 * j + 1 < SB) continue;  // blocks t < s only
                     const X4 lo = 2 * j >= SB ? sm.f1[tix(2 * j, SB)][lane] : z4;
                     const X4 hi = sm.f1[tix(2 * j + 1, SB)][lane];
-                    accA = mma(gyf[j], cat<X8, X4>(lo, hi), accA);
+                    accA = mma(tok_frag(sm.gy, 32 * j + 4 * g, 32 * j + 16 + 4 * g, w4, lane),
+                               cat<X8, X4>(lo, hi), accA);
                 }
 #pragma unroll
                 for (int kk = 0; kk < KN; ++kk) accG = mma(gf[kk], tile_frag<N>(sm.bs, 16 * SB + l16, kk, g), accG);
@@ -372,10 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
                 f32x4 raw;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) raw[i] = accA[i] + wl * accG[i];
-                if (s < clen) store4((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * wave + 4 * g, ds * raw);
-                const X4 xv = tld4(sm.xs, s, wave, 4 * g);
-                const X4 gv = tld4(sm.gy, s, wave, 4 * g);
-                const X4 yv = tld4(sm.ys, s, wave, 4 * g);
+                if (s < clen) store4((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * w4 + 4 * g, ds * raw);
+                const X4 xv = tld4(sm.xs, s, w4, 4 * g);
+                const X4 gv = tld4(sm.gy, s, w4, 4 * g);
+                const X4 yv = tld4(sm.ys, s, w4, 4 * g);
                 float dw = 0.f, zx = 0.f, yy = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -387,28 +448,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
                 zx = xor_add(xor_add(zx, 16), 32);
                 yy = xor_add(xor_add(yy, 16), 32);
                 if (g == 0) {
-                    sm.red[0][wave][s] = dw;
-                    sm.red[1][wave][s] = zx;
-                    sm.red[2][wave][s] = yy;
+                    sm.red[0][w4][s] = dw;
+                    sm.red[1][w4][s] = zx;
+                    sm.red[2][w4][s] = yy;
                 }
             }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const X4 gv = ld4(sm.gr + ((wave * NB + nb) * 64 + lane) * 4);
-                const X4 hv = ld4(sm.hr + ((wave * NB + nb) * 64 + lane) * 4);
+            for (int i = 0; i < NBH; ++i) {
+                const int nb = q * NBH + i;
+                if (nb >= NB) break;
+                const X4 gv = ld4(sm.gr + srun((w4 * NB + nb) * 64 + lane));
+                const X4 hv = ld4(sm.hr + srun((w4 * NB + nb) * 64 + lane));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gh += (float)gv[i] * (float)hv[i];
+                for (int k = 0; k < 4; ++k) gh += (float)gv[k] * (float)hv[k];
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 3; ++k) sm.red[k][wave][lane] = 0.f;
+            for (int k = 0; k < 3; ++k)
+                if (lane < 32) sm.red[k][w4][32 * q + lane] = 0.f;
         }
         gh = wave_prefix_sum(gh);
         if (lane == 63) sm.gh[wave] = gh;
 
-        // dB for tokens s in block `wave`: d_s sum_t A2[t][s] C_t + w_s Gout X_s
+        // dB for tokens s in block w4: d_s sum_t A2[t][s] C_t + w_s Gout X_s
         {
-            const int SB = wave;
+            const int SB = w4;
             X8 a2[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -422,19 +486,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
 #pragma unroll
             for (int kp = 0; kp < 2; ++kp) xw[kp] = scale8<T>(tile_frag<kPGroup>(sm.xs, s, kp, g), ws);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int i = 0; i < NBH; ++i) {
+                const int nb = q * NBH + i;
+                if (nb >= NB) break;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     if (2 * j + 1 >= SB)
-                        dBt[nb] = mma(tok_frag(sm.cs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a2[j], dBt[nb]);
+                        dBt[i] = mma(tok_frag(sm.cs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a2[j], dBt[i]);
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
-                    dBt[nb] = mma(state_frag_t<NB>(sm.gr, nb, kp, g, lane), xw[kp], dBt[nb]);
+                    dBt[i] = mma(state_frag_t<NB>(sm.gr, nb, kp, g, lane), xw[kp], dBt[i]);
             }
         }
-        // dC for tokens t in block `wave`: sum_s A2[t][s] d_s B_s + e^{cs_t} Hprev dy_t
+        // dC for tokens t in block w4: sum_s A2[t][s] d_s B_s + e^{cs_t} Hprev dy_t
         {
-            const int TB = wave;
+            const int TB = w4;
             X8 a3[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -448,14 +514,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
 #pragma unroll
             for (int kp = 0; kp < 2; ++kp) gw[kp] = scale8<T>(tile_frag<kPGroup>(sm.gy, t, kp, g), fe);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
+            for (int i = 0; i < NBH; ++i) {
+                const int nb = q * NBH + i;
+                if (nb >= NB) break;
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     if (2 * j <= TB)
-                        dCt[nb] = mma(tok_frag(sm.bs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a3[j], dCt[nb]);
+                        dCt[i] = mma(tok_frag(sm.bs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a3[j], dCt[i]);
 #pragma unroll
                 for (int kp = 0; kp < 2; ++kp)
-                    dCt[nb] = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], dCt[nb]);
+                    dCt[i] = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], dCt[i]);
             }
         }
         block_sync();
@@ -469,8 +537,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
                 dw += sm.red[0][w][s];
                 zx += sm.red[1][w][s];
                 yy += sm.red[2][w][s];
-                ghs += sm.gh[w];
             }
+#pragma unroll
+            for (int w = 0; w < kBWaves; ++w) ghs += sm.gh[w];
             const bool in = s < clen;
             const float ds = D.dt[s];
             // <Gout, Hend>: e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last - cs_s} d_s zx_s
@@ -486,15 +555,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_chunk_kernel(BParams p) {
         block_sync();  // every read of this head's LDS is done
     }
 
-    // this subset's partial dB (s block `wave`) and dC (t block `wave`)
+    // this subset's partial dB (s block w4) and dC (t block w4), state rows of half q
     {
-        const int s = 16 * wave + l16;
+        const int s = 16 * w4 + l16;
         if (s < clen) {
             const int64_t o = ((int64_t)sub * p.ntok + tok(s)) * GN + grp * N + 4 * g;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                *(f32x4*)(p.dB_part + o + 16 * nb) = dBt[nb];
-                *(f32x4*)(p.dC_part + o + 16 * nb) = dCt[nb];
+            for (int i = 0; i < NBH; ++i) {
+                const int nb = q * NBH + i;
+                if (nb >= NB) break;
+                *(f32x4*)(p.dB_part + o + 16 * nb) = dBt[i];
+                *(f32x4*)(p.dC_part + o + 16 * nb) = dCt[i];
             }
         }
     }
@@ -541,7 +612,7 @@ template <typename T, int N>
 hipError_t launch_bwd_t(const BParams& p, hipStream_t s) {
     const int64_t grid = p.nchunk * p.G * p.nsub;
     if (grid > 0)
-        hipLaunchKernelGGL((bwd_chunk_kernel<T, N>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<T, N>), dim3((unsigned)grid), dim3(kBThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -113,6 +113,12 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s);
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s);
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
+// The backward pass's two chunk-state passes (pa: kModeState on (B, x), pb:
+// weights e^{cs} on (C, dy); same sizes, one head per workgroup) and their two
+// state passes, each pair in one launch.
+hipError_t launch_span_state_pair(const KParams& pa, const KParams& pb, int dtype, int N,
+                                  hipStream_t s);
+hipError_t launch_state_pass_pair(const KParams& pa, const KParams& pb, int dtype, hipStream_t s);
 
 // Head-wave kernels (ssd_hw_kernels.hip): bf16, d_state 64 or 128; hg heads
 // per workgroup (1, 2, 4), npb 16-column blocks per wave (2, 4).

@@ -201,8 +201,8 @@ __device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" :
 //              its span, and writes y.  The last span of a sequence skips the
 //              local state (no later span reads it) and writes final_state.
 template <typename T, int N, int HG, int MODE>
-__global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) void span_kernel(
-    KParams p) {
+__device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
+                                          Smem<T, N, HG, !is_state(MODE)>& sm) {
     using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
@@ -210,7 +210,6 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
     constexpr int W = 16 / EPU;               // 16-byte units per block row
     constexpr int XI = 4 * W, BI = NB * W;    // load instructions per X / B / C tile
     constexpr bool SCANL = !is_state(MODE);  // LDS holds the scan buffers
-    __shared__ Smem<T, N, HG, SCANL> sm;
 
     const int hg = is_state(MODE) ? p.hg_state : p.hg_scan;
     const int ngrp = (p.H + hg - 1) / hg;
@@ -227,7 +226,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
         // which tags its flags.  The chain's last workgroup resets the count
         // and advances the epoch for the next launch.
         const int64_t per_seq = (int64_t)ngrp * p.npg;
-        const int64_t chain = blockIdx.x / p.sps;
+        const int64_t chain = blk / p.sps;
         if (tid == 0) {
             const uint64_t te = __hip_atomic_fetch_add((uint64_t*)(p.sync + kSyncHeader) + chain, 1ull,
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -248,7 +247,7 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
         // XCD-aware order: consecutive logical blocks (same span, neighbouring
         // head groups, which share B and C) land on the same XCD and its L2.
         const int64_t per = (nreal + kXcds - 1) / kXcds;
-        const int64_t bid = blockIdx.x;
+        const int64_t bid = blk;
         logical = (bid % kXcds) * per + bid / kXcds;
         if (logical >= nreal) return;
     }
@@ -670,13 +669,32 @@ __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) 
     }
 }
 
+template <typename T, int N, int HG, int MODE>
+__global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) void span_kernel(
+    KParams p) {
+    __shared__ Smem<T, N, HG, !is_state(MODE)> sm;
+    span_body<T, N, HG, MODE>(p, blockIdx.x, sm);
+}
+
+// The backward pass's two chunk-state passes in one launch (they are
+// independent): workgroups below na form the states of the forward
+// direction from (B, x), the rest the output-gradient states from (C, dy).
+// na is a multiple of the XCD count, so each half keeps its XCD-aware order.
+template <typename T, int N>
+__global__ __launch_bounds__(kThreads, (span_occupancy<T, N, 1, kModeState>())) void span_state_pair_kernel(
+    KParams pa, KParams pb, int64_t na) {
+    __shared__ Smem<T, N, 1, false> sm;
+    if ((int64_t)blockIdx.x < na) span_body<T, N, 1, kModeState>(pa, blockIdx.x, sm);
+    else span_body<T, N, 1, kModeStateGrad>(pb, blockIdx.x - na, sm);
+}
+
 // Walk the spans of one sequence for V = 16 bytes of consecutive stored
 // state entries: replace each span state S_k (input type) by the state
 // entering the span and carry H <- decay_k H + S_k in fp32; H after the last
 // span is the final state.  Stored entry o of a (span, head) block holds
 // state (n, p) as laid out by state_off(); init/final are [N][P].
 template <typename TS>
-__global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
+__device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     constexpr int U = 8;                 // spans in flight per thread
     constexpr int V = 16 / sizeof(TS);   // state entries per thread
     typedef TS TSV __attribute__((ext_vector_type(V)));
@@ -684,7 +702,6 @@ __global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
     const int N = p.N, NB = p.N / 16;
     const int EV = p.P * N / V;
     const int64_t S = p.nseq ? p.nseq : p.batch;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= S * p.H * EV) return;
     const int ev = (int)(gid % EV);
     const int h = (int)((gid / EV) % p.H);
@@ -743,6 +760,19 @@ __global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < V; ++j) p.final_state[hb + idx[j]] = run[j];
     }
+}
+
+template <typename TS>
+__global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
+    state_pass_body<TS>(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// Two independent state passes in one launch: workgroups below na walk pa's
+// spans, the rest pb's.
+template <typename TS>
+__global__ __launch_bounds__(256) void state_pass_pair_kernel(KParams pa, KParams pb, int64_t na) {
+    if ((int64_t)blockIdx.x < na) state_pass_body<TS>(pa, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    else state_pass_body<TS>(pb, ((int64_t)blockIdx.x - na) * 256 + threadIdx.x);
 }
 
 // One workgroup: sanitize cu_seqlens (clamped running maximum, first entry
@@ -897,6 +927,47 @@ hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s) 
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s) {
     return p.fuse_pass == 2 ? launch_span<kModeFused>(p, dtype, N, s)
                             : launch_span<kModeScan>(p, dtype, N, s);
+}
+
+hipError_t launch_span_state_pair(const KParams& pa, const KParams& pb, int dtype, int N,
+                                  hipStream_t s) {
+    const int64_t n = pa.nspan * pa.H * pa.npg;  // one head per workgroup (both halves)
+    if (n == 0) return hipSuccess;
+    const int64_t na = (n + kXcds - 1) / kXcds * kXcds;
+#define SSD_PAIR(T, NN) \
+    hipLaunchKernelGGL((span_state_pair_kernel<T, NN>), dim3((unsigned)(2 * na)), dim3(kThreads), 0, s, pa, pb, na)
+    if (dtype == 1) {
+        switch (N) {
+            case 16: SSD_PAIR(bf16, 16); break;
+            case 32: SSD_PAIR(bf16, 32); break;
+            case 64: SSD_PAIR(bf16, 64); break;
+            case 128: SSD_PAIR(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (N) {
+            case 16: SSD_PAIR(float, 16); break;
+            case 32: SSD_PAIR(float, 32); break;
+            case 64: SSD_PAIR(float, 64); break;
+            case 128: SSD_PAIR(float, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef SSD_PAIR
+    return hipGetLastError();
+}
+
+hipError_t launch_state_pass_pair(const KParams& pa, const KParams& pb, int dtype, hipStream_t s) {
+    const int64_t S = pa.nseq ? pa.nseq : pa.batch;
+    const int V = dtype == 1 ? 8 : 4;
+    const int64_t n = S * pa.H * (int64_t)pa.P * pa.N / V;
+    if (n == 0) return hipSuccess;
+    const int64_t na = (n + 255) / 256;
+    if (dtype == 1)
+        hipLaunchKernelGGL(state_pass_pair_kernel<bf16>, dim3((unsigned)(2 * na)), dim3(256), 0, s, pa, pb, na);
+    else
+        hipLaunchKernelGGL(state_pass_pair_kernel<float>, dim3((unsigned)(2 * na)), dim3(256), 0, s, pa, pb, na);
+    return hipGetLastError();
 }
 
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s) {

@@ -217,7 +217,7 @@ def test_bwd_workspace_bytes(m):
 
 def test_bwd_head_subsets(m, monkeypatch):
     """The gradient kernel's head subsets: the largest divisor of the group's
-    heads that keeps >= 512 workgroups -- fewer subsets, smaller partials."""
+    heads that keeps >= 256 workgroups (one per CU) -- fewer subsets, smaller partials."""
     few = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))   # 1024 chunks
     monkeypatch.setenv("SSD_BWD_HEADS", "1")
     many = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))
