@@ -47,6 +47,15 @@ STAGE_KERNEL = {"state": "span_kernel<bf16, N, 1, kModeState>", "pass": "state_p
                 "fused": "span_kernel<bf16, N, 1, kModeFused>", "table": "span_table_kernel"}
 
 
+def kernel_label(stage: str, plan, w) -> str:
+    """Name of the kernel that runs a stage under this plan."""
+    if plan.head_wave and stage in ("state", "scan"):
+        mode = 1 if stage == "scan" else 0
+        return (f"hw_span_kernel<{w.d_state}, {plan.heads_per_wg}, "
+                f"{plan.cols_per_wave // 16}, {mode}>")
+    return STAGE_KERNEL[stage]
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -262,7 +271,7 @@ def main() -> int:
                                f"{w.dtype} in / fp32 state" + (", fwd+rev" if w.bidir else ""),
                    "global_batch": w.batch, "seq_len": w.seqlen, "parallelism": "single-gpu",
                    "chunks_per_span": plan.chunks_per_span},
-        "roofline": {"bound": "hbm", "kernel": STAGE_KERNEL[dom],
+        "roofline": {"bound": "hbm", "kernel": kernel_label(dom, plan, w),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
