@@ -215,14 +215,14 @@ int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
     const int32_t hpg = d->nheads / d->ngroups;
     int32_t hs = 1;
     for (int32_t v = hpg; v >= 1; --v) {
-        if (hpg % v == 0 && bp->nchunk * d->ngroups * (hpg / v) >= 256) {
+        if (hpg % v == 0 && v <= ssd::kBwdMaxHeads && bp->nchunk * d->ngroups * (hpg / v) >= 256) {
             hs = v;
             break;
         }
     }
     if (const char* e = getenv("SSD_BWD_HEADS")) {
         const int v = atoi(e);
-        if (v >= 1 && v <= hpg && hpg % v == 0) hs = v;
+        if (v >= 1 && v <= hpg && v <= ssd::kBwdMaxHeads && hpg % v == 0) hs = v;
     }
     bp->hs = hs;
     bp->nsub = hpg / hs;

@@ -113,11 +113,24 @@ struct __attribute__((aligned(16))) BSmem {
     X4 f1[kTiles][64];         // (C B^T) o L, rows t: B operand of dy^T A1
     X4 f2[kTiles][64];         // (dy X^T) o L, times d_s, rows t: dB
     X4 f3[kTiles][64];         // the same product transposed (rows s): dC
-    BDecay dec;
+    BDecay dec[3];                 // factors of the last, this and the next head
+    __attribute__((aligned(16))) uint32_t dr[kBwdMaxHeads][kChunk];  // d_raw of every head of the workgroup
     float red[3][kWaves][kChunk];  // per-wave partial dw, zx, dy.y
     float gh[8];                   // per-wave partial <Gout, Hprev>
-    __attribute__((aligned(16))) uint32_t dr[kChunk];
 };
+
+// One element stored with an inline-asm store: the compiler's wait counting
+// then sees no stores in the head loop, so the next head's prefetch loads
+// do not wait for this head's output stores to be acknowledged (vector
+// memory operations retire in issue order, so every wait it places for its
+// loads stays sufficient).
+__device__ __forceinline__ void store1_async(bf16* p, float v) {
+    const bf16 o = (bf16)v;
+    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(o) : "memory");
+}
+__device__ __forceinline__ void store1_async(float* p, float v) {
+    asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
 
 // An operand fragment with every element times f, rounded back to T.
 template <typename T>
@@ -287,6 +300,14 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                                                          dir * GN, wave, clen, N, lane);
     issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
                                                          dir * GN, wave, clen, N, lane);
+    // d_raw of every head of the subset, one token per lane (a bf16 value in
+    // the low half of its 32-bit slot)
+    for (int i = wave; i < h1 - h0; i += kBWaves) {
+        const void* src = (const void*)((const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h0 + i);
+        auto* lds = (__attribute__((address_space(3))) void*)sm.dr[i];
+        if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
+        else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+    }
     vm_wait<0>();
     block_sync();
     // C B^T once for the group: block (tb, sb) = rows t, columns s
@@ -304,7 +325,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
 #pragma unroll
     for (int i = 0; i < NBH; ++i) dBt[i] = dCt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ddi = 0.f;
-    const BDecay& D = sm.dec;
     const X4 z4 = {};
 
     // A head's X, dy and y tiles, its two states and its d_raw go through
@@ -317,7 +337,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     constexpr int TI = (4 * W + kBWaves - 1) / kBWaves;  // tile units per lane
     constexpr int SI = (kPGroup * N * (int)sizeof(T) / 1024 + kBWaves - 1) / kBWaves;  // state units
     u32x4 rx[TI], ry[TI], ryy[TI], rg[SI], rh[SI];
-    uint32_t rdr = 0;
     auto tile_off = [&](int i, int64_t rstride) -> int64_t {
         const int j = (i % W) * 64 + lane;
         const int pr = j / W, pu = j % W;
@@ -348,13 +367,15 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 rh[k] = *(const u32x4*)((const T*)p.hprev + hb + o);
             }
         }
-        if (wave == 0) {
-            const T* src = (const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h;
-            if constexpr (sizeof(T) == 2) rdr = *(const uint16_t*)src;
-            else rdr = *(const uint32_t*)src;
-        }
     };
+    // One full wait, outside every branch: the prefetched registers are
+    // needed now, and the compiler's wait placement then knows that nothing
+    // is in flight when the next head's loads go out (its own waits inside
+    // the branches below would otherwise leave loads "pending" at the merge
+    // and put a full wait in the middle of the next fetch).  Every store
+    // still in flight here was issued a whole head earlier.
     auto stash = [&]() {
+        vm_wait<0>();
 #pragma unroll
         for (int k = 0; k < TI; ++k) {
             const int i = wave + kBWaves * k;
@@ -374,33 +395,82 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 *(u32x4*)(sm.hr + so) = rh[k];
             }
         }
-        if (wave == 0) sm.dr[lane] = rdr;
     };
+    // The decay factors of head h + 1 are formed during head h's masking by
+    // the last wave, into slot (h + 1) % 3; the first wave turns head h's
+    // per-token sums into d d_raw during head h + 1's masking (slot h % 3 is
+    // still intact then).  Both mask one block less than the other waves.
+    constexpr int kFW = kBWaves - 1;
     fetch(h0);
+    if (wave == kFW) bwd_factors<T>(sm.dec[0], sm.dr[0][lane], p.d_init, clen, lane);
+
+    // d d_raw of head h is stored after head h + 1's data has arrived (so
+    // the stash's full wait never waits for a store just issued)
+    float dd_val = 0.f;
+    int64_t dd_at = -1;
+    auto store_dd = [&]() {
+        if (dd_at >= 0) store1_async((T*)p.dd_raw + dd_at, dd_val);
+    };
+
+    // per-token sums of head h -> d d_raw (wave 0, lane = token)
+    auto tail = [&](int h) {
+        const BDecay& D = sm.dec[(h - h0) % 3];
+        store_dd();
+        const int s = lane;
+        float dw = 0.f, zx = 0.f, yy = 0.f, ghs = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            dw += sm.red[0][w][s];
+            zx += sm.red[1][w][s];
+            yy += sm.red[2][w][s];
+        }
+#pragma unroll
+        for (int w = 0; w < kBWaves; ++w) ghs += sm.gh[w];
+        const bool in = s < clen;
+        const float ds = D.dt[s];
+        // <Gout, Hend>: e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last - cs_s} d_s zx_s
+        const float ez = lane_value(wave_prefix_sum(in ? D.wl[s] * ds * zx : 0.f), 63);
+        const float E = D.fe[kChunk - 1] * ghs + ez;
+        const float r = in ? yy - ds * dw : 0.f;
+        const float incl = wave_prefix_sum(r);
+        const float da = E + lane_value(incl, 63) - incl + r;  // E + sum_{j >= s} r_j
+        const float gr = (dw - da) * D.sg[s];
+        dd_val = gr;
+        dd_at = in ? tok(s) * p.H + h : -1;
+        ddi += in ? gr : 0.f;
+    };
 
     for (int h = h0; h < h1; ++h) {
+        const BDecay& D = sm.dec[(h - h0) % 3];
         stash();
         block_sync();
         if (h + 1 < h1) fetch(h + 1);
-        if (wave == 0) bwd_factors<T>(sm.dec, sm.dr[lane], p.d_init, clen, lane);
-        block_sync();
 
-        // masked blocks: A1 = (C B^T) o L; A2 = (dy X^T) o L d_s in both orientations
-        for (int ti = wave; ti < kTiles; ti += kBWaves) {
+        if (wave == 0 && h > h0) tail(h - 1);
+
+        // masked blocks, 30 units (block ti, kind): A1 = (C B^T) o L; A2 =
+        // (dy X^T) o L d_s in both orientations; wave w takes units w - 1,
+        // w + 7, ... (the first and the last wave three, the others four)
+        for (int u = (wave + kBWaves - 1) % kBWaves; u < 3 * kTiles; u += kBWaves) {
+            const int kind = u / kTiles, ti = u % kTiles;
             int TB, SB;
             tile_of(ti, TB, SB);
-            sm.f1[ti][lane] = mask_ts<T>(sm.cb[ti][lane], D, TB, SB, lane, clen, false);
-            f32x4 m = {0.f, 0.f, 0.f, 0.f}, mt = {0.f, 0.f, 0.f, 0.f};
+            if (kind == 0) {
+                sm.f1[ti][lane] = mask_ts<T>(sm.cb[ti][lane], D, TB, SB, lane, clen, false);
+            } else {
+                f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                const X8 yt = tile_frag<kPGroup>(sm.gy, 16 * TB + l16, kp, g);
-                const X8 xs = tile_frag<kPGroup>(sm.xs, 16 * SB + l16, kp, g);
-                m = mma(yt, xs, m);
-                mt = mma(xs, yt, mt);
+                for (int kp = 0; kp < 2; ++kp) {
+                    const X8 yt = tile_frag<kPGroup>(sm.gy, 16 * TB + l16, kp, g);
+                    const X8 xs = tile_frag<kPGroup>(sm.xs, 16 * SB + l16, kp, g);
+                    m = kind == 1 ? mma(yt, xs, m) : mma(xs, yt, m);
+                }
+                if (kind == 1) sm.f2[ti][lane] = mask_ts<T>(m, D, TB, SB, lane, clen, true);
+                else sm.f3[ti][lane] = mask_st<T>(m, D, TB, SB, lane, clen);
             }
-            sm.f2[ti][lane] = mask_ts<T>(m, D, TB, SB, lane, clen, true);
-            sm.f3[ti][lane] = mask_st<T>(mt, D, TB, SB, lane, clen);
         }
+        if (wave == kFW && h + 1 < h1)
+            bwd_factors<T>(sm.dec[(h + 1 - h0) % 3], sm.dr[h + 1 - h0][lane], p.d_init, clen, lane);
         block_sync();
 
         // dX for headdim block w4, token blocks 2q and 2q + 1 (transposed:
@@ -433,7 +503,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 f32x4 raw;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) raw[i] = accA[i] + wl * accG[i];
-                if (s < clen) store4((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * w4 + 4 * g, ds * raw);
+                if (s < clen) store4_async((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * w4 + 4 * g, ds * raw);
                 const X4 xv = tld4(sm.xs, s, w4, 4 * g);
                 const X4 gv = tld4(sm.gy, s, w4, 4 * g);
                 const X4 yv = tld4(sm.ys, s, w4, 4 * g);
@@ -526,33 +596,14 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                     dCt[i] = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], dCt[i]);
             }
         }
-        block_sync();
+        block_sync();  // every read of this head's tiles and states is done
+    }
 
-        // per-token sums -> d d_raw (wave 0, lane = token)
-        if (wave == 0) {
-            const int s = lane;
-            float dw = 0.f, zx = 0.f, yy = 0.f, ghs = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                dw += sm.red[0][w][s];
-                zx += sm.red[1][w][s];
-                yy += sm.red[2][w][s];
-            }
-#pragma unroll
-            for (int w = 0; w < kBWaves; ++w) ghs += sm.gh[w];
-            const bool in = s < clen;
-            const float ds = D.dt[s];
-            // <Gout, Hend>: e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last - cs_s} d_s zx_s
-            const float ez = lane_value(wave_prefix_sum(in ? D.wl[s] * ds * zx : 0.f), 63);
-            const float E = D.fe[kChunk - 1] * ghs + ez;
-            const float r = in ? yy - ds * dw : 0.f;
-            const float incl = wave_prefix_sum(r);
-            const float da = E + lane_value(incl, 63) - incl + r;  // E + sum_{j >= s} r_j
-            const float gr = (dw - da) * D.sg[s];
-            if (in) ((T*)p.dd_raw)[tok(s) * p.H + h] = cvt<T>(gr);
-            ddi += in ? gr : 0.f;
-        }
-        block_sync();  // every read of this head's LDS is done
+
+    block_sync();  // the last head's per-token sums are complete
+    if (wave == 0) {
+        tail(h1 - 1);
+        store_dd();
     }
 
     // this subset's partial dB (s block w4) and dC (t block w4), state rows of half q

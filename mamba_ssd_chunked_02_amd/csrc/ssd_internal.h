@@ -87,6 +87,7 @@ struct BParams {
     int32_t reverse;
     float d_init;
 };
+constexpr int kBwdMaxHeads = 64;  // heads one backward workgroup carries at most
 bool bwd_supported(int dtype, int N);
 hipError_t launch_bwd_chunk(const BParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, float* dd_init,
