@@ -157,6 +157,8 @@ int make_plan(const ssd_dims* d, Plan* pl) {
         if (pl->sps == 0 || pl->hw_npb) pl->fuse = 0;  // head-wave: three launches
         if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) pl->fuse = 1;
     }
+    // The span kernels decode their work items in 32 bits.
+    if (pl->nspan * d->nheads * pl->npg >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
     // The header sits at the start of every plan's workspace; the fused
     // launch's words follow it: one 64-bit ticket/epoch word per chain
     // (sequence, head group, column group), then one flag per workgroup.

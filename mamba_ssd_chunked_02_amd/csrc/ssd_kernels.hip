@@ -251,9 +251,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         logical = (bid % kXcds) * per + bid / kXcds;
         if (logical >= nreal) return;
     }
-    const int pg = (int)(logical % p.npg);
-    const int hgi = (int)((logical / p.npg) % ngrp);
-    const int64_t span = logical / ((int64_t)p.npg * ngrp);
+    // (the host keeps span x head group x column group below 2^31, so the
+    // decode divides in 32 bits)
+    const uint32_t lg32 = (uint32_t)logical, rest = lg32 / (uint32_t)p.npg;
+    const int pg = (int)(lg32 - rest * (uint32_t)p.npg);
+    const uint32_t span32 = rest / (uint32_t)ngrp;
+    const int hgi = (int)(rest - span32 * (uint32_t)ngrp);
+    const int64_t span = span32;
     const int h0 = hgi * hg;
     const int nh = min(hg, p.H - h0);  // hg <= HG divides H/G: one B/C group
 
@@ -267,9 +271,9 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         chunk0 = e.y;
         nck = e.z;
     } else {
-        const int64_t seq = span / p.sps;
-        const int kin = (int)(span - seq * p.sps);
-        start = seq * p.L;
+        const uint32_t seq = span32 / (uint32_t)p.sps;
+        const int kin = (int)(span32 - seq * (uint32_t)p.sps);
+        start = (int64_t)seq * p.L;
         len = p.L;
         const int64_t nch = (len + kChunk - 1) / kChunk;
         chunk0 = kin * p.K;
@@ -334,14 +338,17 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
     };
 
-    const int kin = (int)(span % (p.sps > 0 ? p.sps : 1));  // span within its sequence
+    // span within its sequence, and the sequence (batch mode; varlen never
+    // folds or reads these)
+    const uint32_t seq_of = p.sps > 0 ? span32 / (uint32_t)p.sps : span32;
+    const int kin = (int)(span32 - seq_of * (uint32_t)(p.sps > 0 ? p.sps : 1));
     const bool folds = MODE == kModeFused || (MODE == kModeScan && p.fuse_pass);
     const bool write_final = folds && p.final_state && kin == p.sps - 1;
     // (n, p) of this lane's entry i of state block nb, [N][P] offset
     auto np_off = [&](int nb, int i) -> int64_t {
         return (int64_t)(16 * nb + 4 * g + i) * p.P + 16 * pb + l16;
     };
-    const int64_t hseq = ((span - kin) / (p.sps > 0 ? p.sps : 1) * p.H + h) * (int64_t)N * p.P;
+    const int64_t hseq = ((int64_t)seq_of * p.H + h) * (int64_t)N * p.P;
     f32x4 Hs[NB];  // this wave's 16 columns of the state, MFMA result order
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
