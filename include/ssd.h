@@ -189,8 +189,8 @@ int ssd_fwd_stages(uint32_t stage_mask, const ssd_dims* dims,
  * chunked form as ssd_fwd (states entering every chunk, then per-chunk
  * gradients), all in the processing order given by reverse.
  *
- * Built for headdim <= 64 and d_state 16, 32, 64 or 128 (bf16) or 16, 32
- * (float32); other sizes return SSD_ERR_UNSUPPORTED.
+ * Built for d_state 16, 32, 64 or 128 (bf16) or 16, 32 (float32); other
+ * d_state values return SSD_ERR_UNSUPPORTED.  Any headdim ssd_fwd accepts.
  *
  * Arguments as ssd_fwd, plus:
  *   y           the forward output of these inputs (as ssd_fwd wrote it),

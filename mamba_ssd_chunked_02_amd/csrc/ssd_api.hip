@@ -210,7 +210,7 @@ int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
     Plan pl;
     const int st = make_plan(d, &pl);  // the forward's size checks
     if (st != SSD_OK) return st;
-    if (d->headdim > kPGroup || !ssd::bwd_supported(d->dtype, d->d_state)) return SSD_ERR_UNSUPPORTED;
+    if (!ssd::bwd_supported(d->dtype, d->d_state)) return SSD_ERR_UNSUPPORTED;
     const int64_t T = (int64_t)d->batch * d->seqlen;
     bp->cps = (int32_t)ceil_div(d->seqlen, kChunk);
     bp->nchunk = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq : (int64_t)d->batch * bp->cps;
@@ -495,7 +495,7 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     pa.nseq = d.nseq;
     pa.K = 1;
     pa.sps = d.nseq > 0 ? 0 : bp.cps;
-    pa.npg = 1;
+    pa.npg = (int32_t)ceil_div(d.headdim, kPGroup);
     pa.hg_state = pa.hg_scan = 1;
     pa.reverse = reverse;
     pa.sync = (uint32_t*)ws;

@@ -224,8 +224,8 @@ __device__ __forceinline__ float xor_add(float v, int m) {
     return v + __shfl_xor(v, m, 64);
 }
 
-// One workgroup: one chunk, one B/C group, one subset of that group's heads
-// (headdim <= 64), eight waves in two quads (q = wave / 4, w4 = wave % 4).
+// One workgroup: one chunk, one B/C group, one subset of that group's heads,
+// eight waves in two quads (q = wave / 4, w4 = wave % 4).
 // Per head:
 //   its X, dy, y, states and d_raw arrive (prefetched during the previous
 //   head); one wave forms the decay factors; the waves mask the 30 causal
@@ -282,20 +282,17 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     const int hpg = p.H / p.G;
     const int h0 = grp * hpg + sub * p.hs;
     const int h1 = min(h0 + p.hs, (grp + 1) * hpg);
-    const int P = p.P, npb = P / 16, PN = P * N;
     const int GN = p.G * N;
-
-    // zero what no load fills: X / dy / y blocks past the headdim, state
-    // entries past P*N (they meet the zero columns of X and dy in K)
-    for (int i = npb * kChunk * 16 + tid; i < kChunk * kPGroup; i += kBThreads) {
-        sm.xs[i] = cvt<T>(0.f);
-        sm.gy[i] = cvt<T>(0.f);
-        sm.ys[i] = cvt<T>(0.f);
-    }
-    for (int i = PN + tid; i < kPGroup * N; i += kBThreads) {
-        sm.gr[i] = cvt<T>(0.f);
-        sm.hr[i] = cvt<T>(0.f);
-    }
+    // The loop runs over units (head, 64-column group of the headdim), head
+    // by head.  Everything but dx is linear in the contributions of the
+    // column groups -- the only sum over the headdim inside a chunk, dy X^T,
+    // enters every later product linearly, and so do the per-token sums of
+    // the tail -- so each group is a unit of its own: dx is written per
+    // group, dB / dC keep accumulating, and d d_raw adds its groups' parts
+    // before one store per head.
+    const int P = p.P, npg = (P + kPGroup - 1) / kPGroup;
+    const int nunit = (h1 - h0) * npg;
+    auto ucols = [&](int u) { return min(kPGroup, P - kPGroup * (u % npg)); };
     issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.bs, (const T*)p.B + tb0 * GN + grp * N,
                                                          dir * GN, wave, clen, N, lane);
     issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
@@ -345,10 +342,12 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         const int col = (i / W) * 16 + (pu ^ b3) * EPU;
         return clen == kChunk || r < clen ? r * rstride + col : col;
     };
-    auto fetch = [&](int h) {
-        const T* xr = (const T*)p.x + tb0 * p.xs_t + h * p.xs_h;
-        const T* gr = (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h;
-        const T* yr = (const T*)p.y + tb0 * p.ys_t + h * p.ys_h;
+    auto fetch = [&](int u) {
+        const int h = h0 + u / npg, pcol0 = kPGroup * (u % npg);
+        const int npb = ucols(u) / 16, PN = ucols(u) * N;
+        const T* xr = (const T*)p.x + tb0 * p.xs_t + h * p.xs_h + pcol0;
+        const T* gr = (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h + pcol0;
+        const T* yr = (const T*)p.y + tb0 * p.ys_t + h * p.ys_h + pcol0;
 #pragma unroll
         for (int k = 0; k < TI; ++k) {
             const int i = wave + kBWaves * k;
@@ -358,7 +357,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 ryy[k] = *(const u32x4*)(yr + tile_off(i, dir * p.ys_t));
             }
         }
-        const int64_t hb = (chunk * p.H + h) * (int64_t)PN;
+        const int64_t hb = (chunk * p.H + h) * (int64_t)P * N + (int64_t)pcol0 * N;
 #pragma unroll
         for (int k = 0; k < SI; ++k) {
             const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
@@ -374,47 +373,55 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     // the branches below would otherwise leave loads "pending" at the merge
     // and put a full wait in the middle of the next fetch).  Every store
     // still in flight here was issued a whole head earlier.
-    auto stash = [&]() {
+    // Blocks past the unit's columns and state entries past its share are
+    // written as zeros (they meet the zero columns of X and dy in K).
+    auto stash = [&](int u) {
         vm_wait<0>();
+        const int npb = ucols(u) / 16, PN = ucols(u) * N;
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < TI; ++k) {
             const int i = wave + kBWaves * k;
-            if (i < 4 * W && i / W < npb) {
+            if (i < 4 * W) {
                 const int o = (i * 64 + lane) * EPU;
-                *(u32x4*)(sm.xs + o) = rx[k];
-                *(u32x4*)(sm.gy + o) = ry[k];
-                *(u32x4*)(sm.ys + o) = ryy[k];
+                const bool in = i / W < npb;
+                *(u32x4*)(sm.xs + o) = in ? rx[k] : z;
+                *(u32x4*)(sm.gy + o) = in ? ry[k] : z;
+                *(u32x4*)(sm.ys + o) = in ? ryy[k] : z;
             }
         }
 #pragma unroll
         for (int k = 0; k < SI; ++k) {
             const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
-            if (o < PN) {
+            if (o < kPGroup * N) {
                 const int so = srun(o / 4);  // the chunk's first run (EPU/4 runs, adjacent)
-                *(u32x4*)(sm.gr + so) = rg[k];
-                *(u32x4*)(sm.hr + so) = rh[k];
+                *(u32x4*)(sm.gr + so) = o < PN ? rg[k] : z;
+                *(u32x4*)(sm.hr + so) = o < PN ? rh[k] : z;
             }
         }
     };
-    // The decay factors of head h + 1 are formed during head h's masking by
-    // the last wave, into slot (h + 1) % 3; the first wave turns head h's
-    // per-token sums into d d_raw during head h + 1's masking (slot h % 3 is
-    // still intact then).  Both mask one block less than the other waves.
+    // The decay factors of unit u + 1 are formed during unit u's masking by
+    // the last wave, into slot (u + 1) % 3; the first wave turns unit u's
+    // per-token sums into its part of d d_raw during unit u + 1's masking
+    // (slot u % 3 is still intact then).  Both mask one block less than the
+    // other waves.
     constexpr int kFW = kBWaves - 1;
-    fetch(h0);
+    fetch(0);
     if (wave == kFW) bwd_factors<T>(sm.dec[0], sm.dr[0][lane], p.d_init, clen, lane);
 
-    // d d_raw of head h is stored after head h + 1's data has arrived (so
+    // d d_raw of a head is stored after the next unit's data has arrived (so
     // the stash's full wait never waits for a store just issued)
-    float dd_val = 0.f;
+    float dd_acc = 0.f, dd_val = 0.f;
     int64_t dd_at = -1;
     auto store_dd = [&]() {
         if (dd_at >= 0) store1_async((T*)p.dd_raw + dd_at, dd_val);
+        dd_at = -1;
     };
 
-    // per-token sums of head h -> d d_raw (wave 0, lane = token)
-    auto tail = [&](int h) {
-        const BDecay& D = sm.dec[(h - h0) % 3];
+    // per-token sums of unit u -> its part of d d_raw (wave 0, lane = token)
+    auto tail = [&](int u) {
+        const int h = h0 + u / npg;
+        const BDecay& D = sm.dec[u % 3];
         store_dd();
         const int s = lane;
         float dw = 0.f, zx = 0.f, yy = 0.f, ghs = 0.f;
@@ -435,18 +442,22 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         const float incl = wave_prefix_sum(r);
         const float da = E + lane_value(incl, 63) - incl + r;  // E + sum_{j >= s} r_j
         const float gr = (dw - da) * D.sg[s];
-        dd_val = gr;
-        dd_at = in ? tok(s) * p.H + h : -1;
+        dd_acc = u % npg == 0 ? gr : dd_acc + gr;
+        if (u % npg == npg - 1) {
+            dd_val = dd_acc;
+            dd_at = in ? tok(s) * p.H + h : -1;
+        }
         ddi += in ? gr : 0.f;
     };
 
-    for (int h = h0; h < h1; ++h) {
-        const BDecay& D = sm.dec[(h - h0) % 3];
-        stash();
+    for (int u = 0; u < nunit; ++u) {
+        const int h = h0 + u / npg, pcol0 = kPGroup * (u % npg), npb = ucols(u) / 16;
+        const BDecay& D = sm.dec[u % 3];
+        stash(u);
         block_sync();
-        if (h + 1 < h1) fetch(h + 1);
+        if (u + 1 < nunit) fetch(u + 1);
 
-        if (wave == 0 && h > h0) tail(h - 1);
+        if (wave == 0 && u > 0) tail(u - 1);
 
         // masked blocks, 30 units (block ti, kind): A1 = (C B^T) o L; A2 =
         // (dy X^T) o L d_s in both orientations; wave w takes units w - 1,
@@ -469,8 +480,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 else sm.f3[ti][lane] = mask_st<T>(m, D, TB, SB, lane, clen);
             }
         }
-        if (wave == kFW && h + 1 < h1)
-            bwd_factors<T>(sm.dec[(h + 1 - h0) % 3], sm.dr[h + 1 - h0][lane], p.d_init, clen, lane);
+        if (wave == kFW && u + 1 < nunit)
+            bwd_factors<T>(sm.dec[(u + 1) % 3], sm.dr[(u + 1) / npg][lane], p.d_init, clen, lane);
         block_sync();
 
         // dX for headdim block w4, token blocks 2q and 2q + 1 (transposed:
@@ -503,7 +514,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 f32x4 raw;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) raw[i] = accA[i] + wl * accG[i];
-                if (s < clen) store4_async((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + 16 * w4 + 4 * g, ds * raw);
+                if (s < clen)
+                    store4_async((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + pcol0 + 16 * w4 + 4 * g, ds * raw);
                 const X4 xv = tld4(sm.xs, s, w4, 4 * g);
                 const X4 gv = tld4(sm.gy, s, w4, 4 * g);
                 const X4 yv = tld4(sm.ys, s, w4, 4 * g);
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
 
     block_sync();  // the last head's per-token sums are complete
     if (wave == 0) {
-        tail(h1 - 1);
+        tail(nunit - 1);
         store_dd();
     }
 

@@ -208,7 +208,7 @@ def test_bwd_workspace_bytes(m):
     states = 2 * 64 * 24 * 64 * 128 * 2
     assert states < ws < states + 2 * 24 * 4096 * 128 * 4 + (1 << 20)
     assert ws % 256 == 0
-    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 128, 64)) == 0      # headdim > 64
+    assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 192, 64)) > 0      # 3 column groups
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 64, 256)) == 0      # d_state 256
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 64, dtype=0)) == 0
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 32, dtype=0)) > 0
@@ -232,7 +232,6 @@ def test_bwd_rejects_bad_arguments(m):
     assert call_bwd(m, ok, dy=None) == -1                                  # NULL_ARG
     assert call_bwd(m, ok, dB=None) == -1
     assert call_bwd(m, ok, y=None) == -1
-    assert call_bwd(m, m.make_dims(1, 128, 2, 128, 128)) == -5             # headdim > 64
     assert call_bwd(m, m.make_dims(1, 128, 2, 64, 256)) == -5
     assert call_bwd(m, m.make_dims(1, 128, 2, 24, 128)) == -2
     assert call_bwd(m, m.make_dims(1, 128, 2, 64, 128, nseq=2)) == -1      # cu_seqlens missing

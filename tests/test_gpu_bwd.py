@@ -74,6 +74,8 @@ SHAPES = [
     (1, 64, 2, 16, 16, 1),
     (1, 65, 3, 48, 32, 1),
     (1, 1, 2, 64, 128, 1),
+    (1, 150, 2, 192, 64, 1),    # three column groups (the bidirectional workload's headdim)
+    (1, 100, 4, 80, 128, 2),    # a partial second column group
 ]
 
 
@@ -121,6 +123,29 @@ def test_bwd_layer_shape(ssd):
     """Layer-shaped problem (24 heads x headdim 64, d_state 128) at 512 tokens."""
     p = random_problem(331, 1, 512, 24, 64, 128, dtype="bf16", d_init=-4.6)
     bwd_case(ssd, p, with_final=False, label="bwd layer-shaped")
+
+
+def test_bwd_bidir_shape_strided(ssd):
+    """The bidirectional workload's head shape (headdim 192, d_state 64) in
+    the reverse direction, with y and dy as the second halves of
+    [b, L, H, 2P] buffers, on 300 tokens x 4 heads."""
+    p = random_problem(341, 1, 300, 4, 192, 64, dtype="bf16", d_init=-4.6)
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    b, L, H, P = p["x"].shape
+    ycat = torch.empty((b, L, H, 2 * P), dtype=torch.bfloat16, device=DEV)
+    ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], reverse=True, y=ycat[..., P:])
+    g = torch.Generator().manual_seed(9)
+    dy = torch.randn((b, L, H, P), generator=g).to(torch.bfloat16)
+    dycat = torch.zeros((b, L, H, 2 * P), dtype=torch.bfloat16)
+    dycat[..., P:] = dy
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], ycat[..., P:],
+                      dycat.to(DEV)[..., P:], reverse=True)
+    torch.cuda.synchronize()
+    ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy, reverse=True)
+    errs = {k: F.rel_err(got[k].float().cpu(), ref[k]) for k in KEYS}
+    print("bwd bidir-shaped rev " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= BWD_TOL[torch.bfloat16], (k, v)
 
 
 def test_bwd_strided_dy_and_y(ssd):
