@@ -22,9 +22,9 @@ HBM before timing starts.  Prints one JSON line:
   this host on the same workload, repeated for ~10 s.
 * bwd                   -- outside the timed region: the backward pass
   (``ssd_bwd``, gradients of every input for a seeded dL/dy and dL/d
-  final_state) on the same workload, W warm-up calls then K calls between
-  two stream synchronizations; null where the backward is not built for
-  the sizes.
+  final_state; one call per direction for the bidirectional workload) on
+  the same workload, W warm-up steps then K steps between two stream
+  synchronizations; null where the backward is not built for the sizes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -283,20 +283,37 @@ def main() -> int:
         "cpu_baseline": None,
     }
     out["bwd"] = None
-    if not args.no_bwd and not w.bidir and m.ssd_bwd_workspace_bytes(calls[0].dims) > 0:
-        y, fin = calls[0].run()
+    if not args.no_bwd and m.ssd_bwd_workspace_bytes(calls[0].dims) > 0:
         g = torch.Generator(device=dev).manual_seed(7)
-        dy = torch.randn(y.shape, generator=g, device=dev).to(y.dtype)
-        dfin = torch.randn(fin.shape, generator=g, device=dev)
-        bcall = m.prepare_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, dy,
-                              init_state=d["init_state"], cu_seqlens=d["cu_seqlens"],
-                              d_final=dfin)
+        bcalls = []
+        if w.bidir:
+            # one backward per direction, y and dy as halves of [b, L, H, 2P]
+            step()
+            dycat = torch.randn(ycat.shape, generator=g, device=dev).to(ycat.dtype)
+            P = d["x"].shape[3]
+            bws = None
+            for rev in (0, 1):
+                bc = m.prepare_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                                   ycat[..., P * rev:P * (rev + 1)],
+                                   dycat[..., P * rev:P * (rev + 1)], reverse=bool(rev),
+                                   workspace=bws)
+                bws = bc.workspace
+                bcalls.append(bc)
+        else:
+            y, fin = calls[0].run()
+            dy = torch.randn(y.shape, generator=g, device=dev).to(y.dtype)
+            dfin = torch.randn(fin.shape, generator=g, device=dev)
+            bcalls.append(m.prepare_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, dy,
+                                        init_state=d["init_state"], cu_seqlens=d["cu_seqlens"],
+                                        d_final=dfin))
         for _ in range(args.warmup):
-            bcall.run()
+            for bc in bcalls:
+                bc.run()
         torch.cuda.synchronize()
         tb = time.perf_counter()
         for _ in range(K):
-            bcall.run()
+            for bc in bcalls:
+                bc.run()
         torch.cuda.synchronize()
         bwd_ms = (time.perf_counter() - tb) / K * 1e3
         out["bwd"] = {"ms_per_step": round(bwd_ms, 5),
