@@ -700,6 +700,17 @@ __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, 1, kModeState>())) 
 // entering the span and carry H <- decay_k H + S_k in fp32; H after the last
 // span is the final state.  Stored entry o of a (span, head) block holds
 // state (n, p) as laid out by state_off(); init/final are [N][P].
+// A 16-byte store the compiler's wait counting does not see (the s_nop
+// covers the hazard of a VALU write to the data registers right after a
+// store of more than 8 bytes).
+template <typename V16>
+__device__ __forceinline__ void store16_async(V16* p, const V16& v) {
+    static_assert(sizeof(V16) == 16, "16-byte vector");
+    typedef uint32_t U4 __attribute__((ext_vector_type(4)));
+    const U4 w = __builtin_bit_cast(U4, v);
+    asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 0" ::"v"(p), "v"(w) : "memory");
+}
+
 template <typename TS>
 __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     constexpr int U = 8;                 // spans in flight per thread
@@ -740,27 +751,44 @@ __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     // span number k of the walk: s0 + k, or s1 - 1 - k walking backwards
     const int64_t ns = s1 - s0;
     auto span_at = [&](int64_t k) { return p.pass_desc ? s1 - 1 - k : s0 + k; };
-    for (int64_t k = 0; k < ns; k += U) {
-        TSV v[U];
-        float d[U];
+    // Two batches of U spans in flight: batch k + U is loaded while batch k
+    // is combined, so a long walk pays about one memory latency per batch
+    // of U spans rather than one per batch plus the combine.  The loads are
+    // branch-free (positions past the walk re-read its last span, unused)
+    // and the stores are issued by store16_async, which the compiler's wait
+    // counting does not see: so the only waits it places are the exact ones
+    // for the batch being combined.  Loads and stores retire in order, so a
+    // wait that counts only loads still covers every load it names.
+    TSV va[U], vb[U];
+    float da[U], db[U];
+    auto load = [&](int64_t k, TSV (&v)[U], float (&d)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k + u < ns) {
-                const int64_t sp = span_at(k + u);
-                v[u] = st[(sp * p.H + h) * EV + ev];
-                d[u] = p.decay[sp * p.H + h];
-            }
+            const int64_t sp = span_at(k + u < ns ? k + u : ns - 1);
+            v[u] = st[(sp * p.H + h) * EV + ev];
+            d[u] = p.decay[sp * p.H + h];
         }
+    };
+    auto combine = [&](int64_t k, const TSV (&v)[U], const float (&d)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k + u < ns) {
-                TSV o;
+            TSV o;
 #pragma unroll
-                for (int j = 0; j < V; ++j) o[j] = (TS)run[j];
-                st[(span_at(k + u) * p.H + h) * EV + ev] = o;
+            for (int j = 0; j < V; ++j) o[j] = (TS)run[j];
+            const bool in = k + u < ns;  // positions past the walk change nothing
+            if (in) store16_async(&st[(span_at(k + u) * p.H + h) * EV + ev], o);
 #pragma unroll
-                for (int j = 0; j < V; ++j) run[j] = d[u] * run[j] + (float)v[u][j];
-            }
+            for (int j = 0; j < V; ++j) run[j] = in ? d[u] * run[j] + (float)v[u][j] : run[j];
+        }
+    };
+    if (ns > 0) {
+        load(0, va, da);
+        for (int64_t k = 0; k < ns; k += 2 * U) {
+            load(k + U, vb, db);
+            combine(k, va, da);
+            if (k + U >= ns) break;
+            load(k + 2 * U, va, da);
+            combine(k + U, vb, db);
         }
     }
     if (p.final_state) {
