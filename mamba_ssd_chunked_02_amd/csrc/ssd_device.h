@@ -240,9 +240,13 @@ __device__ __forceinline__ f32x8 tok_frag(const float* t, int r0, int r1, int bl
 template <int N, typename T>
 __device__ __forceinline__ typename Vec<T>::x8 tile_frag(const T* tile, int r, int kk, int g) {
     using X4 = typename Vec<T>::x4;
-    const X4 lo = tld4(tile, r, 2 * kk, 4 * g);
+    // the hi half sits exactly one column block after the lo half, written
+    // as such so that both come from one base address (one paired read into
+    // the fragment's own registers)
+    const T* const plo = tile + boff<T>(r, 2 * kk, 4 * g);
+    const X4 lo = ld4(plo);
     X4 hi = {};
-    if (N % 32 == 0 || 2 * kk + 1 < N / 16) hi = tld4(tile, r, 2 * kk + 1, 4 * g);
+    if (N % 32 == 0 || 2 * kk + 1 < N / 16) hi = ld4(plo + kChunk * 16);
     return cat<typename Vec<T>::x8, X4>(lo, hi);
 }
 

@@ -695,11 +695,6 @@ __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, 1, kModeState>())) 
     else span_body<T, N, 1, kModeStateGrad>(pb, blockIdx.x - na, sm);
 }
 
-// Walk the spans of one sequence for V = 16 bytes of consecutive stored
-// state entries: replace each span state S_k (input type) by the state
-// entering the span and carry H <- decay_k H + S_k in fp32; H after the last
-// span is the final state.  Stored entry o of a (span, head) block holds
-// state (n, p) as laid out by state_off(); init/final are [N][P].
 // A 16-byte store the compiler's wait counting does not see (the s_nop
 // covers the hazard of a VALU write to the data registers right after a
 // store of more than 8 bytes).
@@ -711,6 +706,11 @@ __device__ __forceinline__ void store16_async(V16* p, const V16& v) {
     asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 0" ::"v"(p), "v"(w) : "memory");
 }
 
+// Walk the spans of one sequence for V = 16 bytes of consecutive stored
+// state entries: replace each span state S_k (input type) by the state
+// entering the span and carry H <- decay_k H + S_k in fp32; H after the last
+// span is the final state.  Stored entry o of a (span, head) block holds
+// state (n, p) as laid out by state_off(); init/final are [N][P].
 template <typename TS>
 __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     constexpr int U = 8;                 // spans in flight per thread
