@@ -40,7 +40,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD chunked-scan fwd Mtokens/s at 1 GPU; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc", "ssd_kernels.hip")
+# sources the span kernels are compiled from (their traffic counters go
+# stale when either changes)
+KERNEL_SRCS = [os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc", f)
+               for f in ("ssd_kernels.hip", "ssd_device.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_layer.json")
 STAGE_KERNEL = {"state": "span_kernel<bf16, N, 1, kModeState>", "pass": "state_pass_kernel",
                 "scan": "span_kernel<bf16, N, 1, kModeScan>",
@@ -57,8 +60,11 @@ def kernel_label(stage: str, plan, w) -> str:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def stage_bytes(w, plan, spans_used: int) -> dict:
