@@ -166,3 +166,16 @@ def test_bwd_strided_dy_and_y(ssd):
                         init_state=p["init_state"])
     for k in KEYS:
         assert F.rel_err(got[k].float().cpu(), ref[k]) <= BWD_TOL[torch.bfloat16], k
+
+
+def test_bwd_long_walks_weak_decay(ssd):
+    """Both chunk-state passes over walks of 1 to 38 chunks (every position of
+    the pass's two batches of eight in flight, walks past two batches), with
+    weak decay so a state carried wrongly anywhere shows in the gradients of
+    the sequence's first tokens and of the initial state."""
+    lens = [64 * 37 + 5, 64 * 16, 1, 64 * 17 - 3, 64 * 9]
+    p = random_problem(347, 1, 0, 2, 16, 16, dtype="f32", lengths=lens, d_init=-6.0,
+                       init_scale=1.0)
+    bwd_case(ssd, p, label="bwd long walks")
+    bwd_case(ssd, p, reverse=True, label="bwd long walks rev")
+

@@ -285,6 +285,20 @@ def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
     check(ssd, q, reverse, label=f"fuse={fuse} f32")
 
 
+def test_state_pass_long_walks(ssd, monkeypatch):
+    """The separate state pass over walks of 1 to 38 spans (one chunk each):
+    every position of its two batches of eight in flight, the tail of a walk
+    inside either batch, and walks longer than two batches; weak decay, so a
+    state carried or dropped wrongly anywhere along a walk shows at its end."""
+    monkeypatch.setenv("SSD_KERNEL", "span")
+    monkeypatch.setenv("SSD_SPAN_CHUNKS", "1")
+    lens = [64 * 37 + 5, 64 * 16, 64 * 17 - 3, 64 * 8, 64 * 9, 1, 64 * 24 + 1]
+    p = random_problem(173, 1, 0, 2, 16, 16, dtype="f32", lengths=lens, d_init=-6.0,
+                       init_scale=1.0)
+    check(ssd, p, False, label="long walks")
+    check(ssd, p, True, label="long walks rev")
+
+
 def _sync_words(ws, chains):
     """Count of timed-out flag waits (header word 2) and each chain's 64-bit
     ticket/epoch word (after the 256-byte header), as (count, epoch) pairs."""
