@@ -19,6 +19,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// An integer from the environment (tuning overrides), or dflt.
+int getenv_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e && e[0] ? atoi(e) : dflt;
+}
+
 struct Plan {
     int32_t K = 1;          // chunks per span
     int32_t sps = 0;        // spans per sequence (batch mode)
@@ -524,7 +530,20 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     pg.decay = (float*)(ws + bp.off_db);
     pg.wmode = 1;
     pg.pass_desc = 1;
-    e = ssd::launch_span_state_pair(pa, pg, d.dtype, d.d_state, s);
+    // In batch mode each chunk-state workgroup walks up to four chunks of a
+    // sequence (its loads double-buffered) and stores every chunk's local
+    // state: the same states as one workgroup per chunk, with a quarter of
+    // the workgroup set-up.
+    ssd::KParams pa4 = pa, pg4 = pg;
+    if (d.nseq == 0 && getenv_int("SSD_BWD_STATE_CHUNKS", 4) == 4) {
+        for (ssd::KParams* k : {&pa4, &pg4}) {
+            k->K = 4;
+            k->sps = (int32_t)ceil_div(bp.cps, 4);
+            k->nspan = (int64_t)d.batch * k->sps;
+            k->chunk_out = 1;
+        }
+    }
+    e = ssd::launch_span_state_pair(pa4, pg4, d.dtype, d.d_state, s);
     if (e == hipSuccess) e = ssd::launch_state_pass_pair(pa, pg, d.dtype, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
 

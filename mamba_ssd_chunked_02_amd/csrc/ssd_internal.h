@@ -56,6 +56,10 @@ struct KParams {
                             // (the backward's output-gradient state)
     int32_t pass_desc;      // state_pass walks each sequence's spans from
                             // its last to its first
+    int32_t chunk_out;      // span_state, batch mode, K <= 4: store the local
+                            // state and decay of every chunk of the span (slot
+                            // seq * chunks-per-sequence + chunk) instead of
+                            // the span's
     float d_init;
 };
 

@@ -356,6 +356,10 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     auto state_ptr = [&](int64_t sp) -> T* {
         return (T*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
     };
+    // (chunk_out) state slot of the span's first chunk: chunks are numbered
+    // per sequence, ceil(L / 64) of them
+    const bool chunk_out = is_state(MODE) && p.chunk_out;
+    const int64_t slot0 = (int64_t)seq_of * ((p.L + kChunk - 1) / kChunk) + chunk0;
     // fused kernel: one flag per work item, after the chains' header words
     uint32_t* const flags = p.sync + kSyncHeader + 2 * (int64_t)p.batch * ngrp * p.npg;
 
@@ -455,7 +459,10 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
             // After chunk c's loads this wave issued, in an active scan wave,
             // exactly four y stores (the previous chunk is full), else nothing.
+            // (chunk_out) after chunk c's loads, an active state wave stored
+            // exactly NB entries of the previous chunk's state.
             if (SCAN && active && c > 0) vm_wait<4>();
+            else if (!SCAN && chunk_out && active && c > 0) vm_wait<NB>();
             else vm_wait<0>();
             block_sync();  // every wave's loads of chunk c are in LDS
             if (c > 0 && c % kWaves == 0) {
@@ -588,6 +595,16 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                     }
                 }
                 if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
+                if (!SCAN && chunk_out) {
+                    // this chunk's local state; the next starts from zero
+                    if (active) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            store4_async(state_ptr(slot0 + c) + state_off(pb, nb, lane, NB), Hs[nb]);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             };
             body(sm.xs[buf][q], sm.bs[buf], sm.cs, sm.xs[buf ^ 1][q], sm.bs[buf ^ 1], sm.cs);
         }
@@ -595,6 +612,12 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
     if constexpr (is_state(MODE)) {
         run(std::false_type{});
+        if (chunk_out) {
+            // chunk w4's decay (its factors are still in slot w4: K <= 4)
+            if (pg == 0 && w4 < nck && live && lane == 0)
+                p.decay[(slot0 + w4) * p.H + h] = fexp2(sm.dec[w4][q].cs2[kChunk - 1]);
+            return;
+        }
         if (active) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) store4(state_ptr(span) + state_off(pb, nb, lane, NB), Hs[nb]);

@@ -178,4 +178,10 @@ def test_bwd_long_walks_weak_decay(ssd):
                        init_scale=1.0)
     bwd_case(ssd, p, label="bwd long walks")
     bwd_case(ssd, p, reverse=True, label="bwd long walks rev")
+    # batch mode: the chunk states come from workgroups that walk four chunks
+    # each (the last span of a sequence shorter, its last chunk ragged)
+    q = random_problem(349, 2, 64 * 37 + 5, 2, 16, 16, dtype="f32", d_init=-6.0,
+                       init_scale=1.0)
+    bwd_case(ssd, q, label="bwd long batch")
+    bwd_case(ssd, q, reverse=True, label="bwd long batch rev")
 
