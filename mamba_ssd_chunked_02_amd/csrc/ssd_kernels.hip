@@ -736,7 +736,10 @@ __device__ __forceinline__ void store16_async(V16* p, const V16& v) {
 // state (n, p) as laid out by state_off(); init/final are [N][P].
 template <typename TS>
 __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
-    constexpr int U = 8;                 // spans in flight per thread
+    // spans per batch.  Two batches of loads (two each per span) and one
+    // batch of stores can be in flight, 5U vector-memory operations, and
+    // the hardware counts at most 63: U = 8 keeps the waits exact.
+    constexpr int U = 8;
     constexpr int V = 16 / sizeof(TS);   // state entries per thread
     typedef TS TSV __attribute__((ext_vector_type(V)));
     typedef float FV __attribute__((ext_vector_type(V)));
