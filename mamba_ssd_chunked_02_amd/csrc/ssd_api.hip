@@ -208,6 +208,8 @@ struct BPlan {
     int32_t cps = 0;       // chunks per sequence (batch mode)
     int32_t nsub = 1, hs = 1;
     size_t off_cu = 0, off_spoff = 0, off_table = 0;
+    int64_t nspan4 = 0;    // (varlen) four-chunk span slots of the chunk-state pass
+    size_t off_cu4 = 0, off_spoff4 = 0, off_table4 = 0;
     size_t off_sa = 0, off_da = 0, off_sb = 0, off_db = 0;
     size_t off_pb = 0, off_pc = 0, off_pi = 0, total = 0;
 };
@@ -245,6 +247,13 @@ int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
         off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
         bp->off_table = off;
         off = align_up(off + (size_t)bp->nchunk * sizeof(int4));
+        bp->nspan4 = ceil_div(T, (int64_t)kChunk * 4) + d->nseq;
+        bp->off_cu4 = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        bp->off_spoff4 = off;
+        off = align_up(off + (size_t)(d->nseq + 1) * sizeof(int32_t));
+        bp->off_table4 = off;
+        off = align_up(off + (size_t)bp->nspan4 * sizeof(int4));
     }
     bp->off_sa = off;
     off = align_up(off + states);
@@ -530,17 +539,32 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     pg.decay = (float*)(ws + bp.off_db);
     pg.wmode = 1;
     pg.pass_desc = 1;
-    // In batch mode each chunk-state workgroup walks up to four chunks of a
-    // sequence (its loads double-buffered) and stores every chunk's local
-    // state: the same states as one workgroup per chunk, with a quarter of
-    // the workgroup set-up.
+    // Each chunk-state workgroup walks up to four chunks of a sequence (its
+    // loads double-buffered) and stores every chunk's local state: the same
+    // states as one workgroup per chunk, with a quarter of the workgroup
+    // set-up.  With cu_seqlens the walks follow a second span table of
+    // four-chunk spans, and the chunk slots are the per-chunk table's.
     ssd::KParams pa4 = pa, pg4 = pg;
-    if (d.nseq == 0 && getenv_int("SSD_BWD_STATE_CHUNKS", 4) == 4) {
+    if (getenv_int("SSD_BWD_STATE_CHUNKS", 4) == 4) {
+        if (d.nseq > 0) {
+            e = ssd::launch_span_table(cu_seqlens, d.nseq, T, 4, bp.nspan4,
+                                       (int32_t*)(ws + bp.off_cu4), (int32_t*)(ws + bp.off_spoff4),
+                                       (int4*)(ws + bp.off_table4), s);
+            if (e != hipSuccess) return SSD_ERR_HIP;
+        }
         for (ssd::KParams* k : {&pa4, &pg4}) {
             k->K = 4;
-            k->sps = (int32_t)ceil_div(bp.cps, 4);
-            k->nspan = (int64_t)d.batch * k->sps;
             k->chunk_out = 1;
+            if (d.nseq > 0) {
+                k->nspan = bp.nspan4;
+                k->cu = (const int32_t*)(ws + bp.off_cu4);
+                k->span_off = (const int32_t*)(ws + bp.off_spoff4);
+                k->table = (const int4*)(ws + bp.off_table4);
+                k->chunk_slot = (const int32_t*)(ws + bp.off_spoff);
+            } else {
+                k->sps = (int32_t)ceil_div(bp.cps, 4);
+                k->nspan = (int64_t)d.batch * k->sps;
+            }
         }
     }
     e = ssd::launch_span_state_pair(pa4, pg4, d.dtype, d.d_state, s);

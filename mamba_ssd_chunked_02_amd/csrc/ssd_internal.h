@@ -56,10 +56,13 @@ struct KParams {
                             // (the backward's output-gradient state)
     int32_t pass_desc;      // state_pass walks each sequence's spans from
                             // its last to its first
-    int32_t chunk_out;      // span_state, batch mode, K <= 4: store the local
-                            // state and decay of every chunk of the span (slot
-                            // seq * chunks-per-sequence + chunk) instead of
-                            // the span's
+    int32_t chunk_out;      // span_state, K <= 4: store the local state and
+                            // decay of every chunk of the span instead of the
+                            // span's, in slot seq * chunks-per-sequence +
+                            // chunk (batch mode) or chunk_slot[seq] + chunk
+                            // (varlen)
+    const int32_t* chunk_slot;  // (varlen, chunk_out) first chunk slot of each
+                                // sequence
     float d_init;
 };
 

@@ -262,10 +262,11 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     const int nh = min(hg, p.H - h0);  // hg <= HG divides H/G: one B/C group
 
     int64_t start, len;
-    int chunk0, nck;
+    int chunk0, nck, vseq = 0;
     if (p.nseq) {
         const int4 e = p.table[span];
         if (e.x < 0) return;
+        vseq = e.x;
         start = p.cu[e.x];
         len = (int64_t)p.cu[e.x + 1] - start;
         chunk0 = e.y;
@@ -356,10 +357,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     auto state_ptr = [&](int64_t sp) -> T* {
         return (T*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
     };
-    // (chunk_out) state slot of the span's first chunk: chunks are numbered
-    // per sequence, ceil(L / 64) of them
+    // (chunk_out) state slot of the span's first chunk: ceil(L / 64) slots
+    // per sequence in batch mode, from the per-chunk table's offsets with
+    // cu_seqlens
     const bool chunk_out = is_state(MODE) && p.chunk_out;
-    const int64_t slot0 = (int64_t)seq_of * ((p.L + kChunk - 1) / kChunk) + chunk0;
+    const int64_t slot0 = !chunk_out ? 0
+                          : p.nseq ? (int64_t)p.chunk_slot[vseq] + chunk0
+                                   : (int64_t)seq_of * ((p.L + kChunk - 1) / kChunk) + chunk0;
     // fused kernel: one flag per work item, after the chains' header words
     uint32_t* const flags = p.sync + kSyncHeader + 2 * (int64_t)p.batch * ngrp * p.npg;
 
