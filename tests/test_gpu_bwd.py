@@ -185,3 +185,30 @@ def test_bwd_long_walks_weak_decay(ssd):
     bwd_case(ssd, q, label="bwd long batch")
     bwd_case(ssd, q, reverse=True, label="bwd long batch rev")
 
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_bwd_chunk_state_walks_bit_exact(ssd, monkeypatch, varlen):
+    """Chunk-state workgroups that walk four chunks (restarting from a zero
+    state at each) do per chunk exactly the arithmetic of one workgroup per
+    chunk: every gradient is bit-identical between the two."""
+    if varlen:
+        p = random_problem(353, 1, 0, 3, 64, 64, dtype="bf16", d_init=-4.6, init_scale=0.5,
+                           lengths=[64 * 9 + 7, 1, 64 * 4, 0, 200])
+    else:
+        p = random_problem(359, 2, 64 * 11 + 30, 3, 64, 64, dtype="bf16", d_init=-4.6,
+                           init_scale=0.5)
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    y, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                       init_state=d["init_state"], cu_seqlens=d["cu_seqlens"])
+    g = torch.Generator().manual_seed(3)
+    dy = torch.randn(p["x"].shape, generator=g).to(torch.bfloat16).to(DEV)
+    out = []
+    for chunks in ("4", "1"):
+        monkeypatch.setenv("SSD_BWD_STATE_CHUNKS", chunks)
+        got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, dy,
+                          init_state=d["init_state"], cu_seqlens=d["cu_seqlens"])
+        torch.cuda.synchronize()
+        out.append(got)
+    for k in KEYS + ("dd_init",):
+        assert torch.equal(out[0][k], out[1][k]), k
