@@ -134,7 +134,7 @@ typedef struct ssd_plan_info {
                                   launch that does STATE, PASS and SCAN
                                   (their workgroups hand span states to each
                                   other); STATE and PASS launch nothing.
-                                  1 is the default in batch mode with 1..16
+                                  1 is the default in batch mode with 1..8
                                   spans per sequence, else 0; the environment
                                   variable SSD_FUSE_PASS=0/1/2 forces one.
                                   Always 0 with head-wave kernels.          */

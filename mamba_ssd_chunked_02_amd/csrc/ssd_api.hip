@@ -50,8 +50,10 @@ int32_t choose_k(int64_t nch, int64_t groups) {
         const int v = atoi(e);
         if (v >= 1 && v <= 64) return v;
     }
+    // Four-chunk spans, or eight when that still leaves >= 1024 span x
+    // head-group items (the wide workload: 8-chunk spans run 15 % faster)
     int32_t K = 4;
-    while (K < 8 && ceil_div(nch, K) * groups >= 4096) K *= 2;
+    while (K < 8 && ceil_div(nch, K) * groups >= 2048) K *= 2;
     return K;
 }
 
@@ -59,8 +61,8 @@ int32_t choose_k(int64_t nch, int64_t groups) {
 // one wave per 32 headdim columns (npb 2) or 64 (npb 4, d_state 64 only).
 // Their per-chunk pipeline is cheaper than the span kernels' but needs long
 // spans to pay for the state pass, so they serve problems with at least
-// 8192 chunk-head-column-group work items (on one MI355X the span kernels
-// are faster below that).  Spans: the longest of 32, 16, ... chunks that
+// 16384 chunk-head-column-group work items (on one MI355X the span kernels
+// are faster below that: 119 vs 146 us on 8192 tokens x 80 heads).  Spans: the longest of 32, 16, ... chunks that
 // still give >= 2048 waves; 4 heads per workgroup at d_state 128 (they share
 // the B / C tiles and the causal C B^T), 2 at d_state 64.
 // SSD_KERNEL=span|hw forces a family; SSD_HW_NPB, SSD_HW_HEADS and
@@ -70,7 +72,7 @@ bool choose_hw(int64_t nch, int64_t heads, int64_t npg, int32_t hpg, int32_t N, 
     const char* kf = getenv("SSD_KERNEL");
     if (kf && strcmp(kf, "span") == 0) return false;
     const bool forced = kf && strcmp(kf, "hw") == 0;
-    if (!forced && nch * heads * npg < 8192) return false;
+    if (!forced && nch * heads * npg < 16384) return false;
     int32_t b = 2;
     auto waves = [&](int32_t k) { return ceil_div(nch, k) * heads * npg * (4 / b); };
     int32_t k = 32;
@@ -148,15 +150,16 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     } else {
         pl->sps = (int32_t)ceil_div(ceil_div(d->seqlen, kChunk), pl->K);
         pl->nspan = (int64_t)d->batch * pl->sps;
-        // Few spans per sequence: span_scan folds the earlier span states of
-        // its sequence itself, which saves the state_pass launch.  Empty
+        // Few spans per sequence (up to 8): span_scan folds the earlier span
+        // states of its sequence itself, which saves the state_pass launch
+        // (with 16 the fold's re-reads cost more than the launch).  Empty
         // sequences keep the three launches (state_pass copies init_state to
         // final_state).  SSD_FUSE_PASS=0 / 1 / 2 forces the three launches,
         // these two, or one fused launch whose workgroups hand the span
         // states to the later spans of their sequence (as fast as the two
         // launches at the sizes measured, so not the default).
         const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
-        pl->fuse = pl->sps > 0 && pl->sps <= ssd::kFuseSpans ? 1 : 0;
+        pl->fuse = pl->sps > 0 && pl->sps <= 8 ? 1 : 0;
         if (const char* e = getenv("SSD_FUSE_PASS")) {
             if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) pl->fuse = e[0] - '0';
         }

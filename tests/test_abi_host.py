@@ -122,7 +122,7 @@ def test_binding_rejects_cpu_mismatch(m):
 
 
 def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
-    """Batch mode with 1..16 spans per sequence folds the state pass into
+    """Batch mode with 1..8 spans per sequence folds the state pass into
     span_scan; packed sequences, longer ones and empty ones keep the three
     launches; SSD_FUSE_PASS forces any of the three plans in batch mode."""
     monkeypatch.delenv("SSD_FUSE_PASS", raising=False)
@@ -131,8 +131,8 @@ def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
     layer_dims = m.make_dims(2, 2048, 24, 64, 128)
     layer = m.ssd_fwd_plan(layer_dims)
     assert layer.chunks_per_span == 4 and layer.fused_pass == 1
-    long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 17, 2, 64, 128))
-    assert long.fused_pass == 0
+    long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 9, 2, 64, 128))
+    assert long.chunks_per_span == 4 and long.fused_pass == 0
     varlen = m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3))
     assert varlen.fused_pass == 0
     assert m.ssd_fwd_plan(m.make_dims(2, 0, 2, 64, 128)).fused_pass == 0
@@ -171,8 +171,8 @@ def test_plan_head_wave_kernels(m, monkeypatch):
             varlen.fused_pass) == (1, 16, 32, 4, 0)
     bidir = m.ssd_fwd_plan(m.make_dims(1, 1 << 20, 8, 192, 64))
     assert (bidir.head_wave, bidir.chunks_per_span, bidir.cols_per_wave, bidir.heads_per_wg) == (1, 32, 32, 2)
-    wide = m.ssd_fwd_plan(m.make_dims(1, 8192, 80, 64, 128))
-    assert (wide.head_wave, wide.chunks_per_span) == (1, 8)
+    wide = m.ssd_fwd_plan(m.make_dims(1, 8192, 80, 64, 128))   # 10240 items: span kernels
+    assert (wide.head_wave, wide.chunks_per_span, wide.fused_pass) == (0, 8, 0)
     assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).head_wave == 0   # layer: span kernels
     assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, dtype=0)).head_wave == 0
     assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 32)).head_wave == 0
