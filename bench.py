@@ -54,7 +54,9 @@ def kernel_label(stage: str, plan, w) -> str:
     """Name of the kernel that runs a stage under this plan."""
     if plan.head_wave and stage in ("state", "scan"):
         mode = 1 if stage == "scan" else 0
-        return (f"hw_span_kernel<{w.d_state}, {plan.heads_per_wg}, "
+        # the state kernel groups at most two heads
+        heads = plan.heads_per_wg if stage == "scan" else min(plan.heads_per_wg, 2)
+        return (f"hw_span_kernel<{w.d_state}, {heads}, "
                 f"{plan.cols_per_wave // 16}, {mode}>")
     return STAGE_KERNEL[stage]
 

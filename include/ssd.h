@@ -142,7 +142,9 @@ typedef struct ssd_plan_info {
                                   product of one head for cols_per_wave
                                   headdim columns); 0: span kernels (four
                                   waves per head, 16 columns each)          */
-    int32_t heads_per_wg;      /* heads sharing one workgroup's B / C tiles  */
+    int32_t heads_per_wg;      /* heads sharing one scan workgroup's B / C
+                                  tiles (a head-wave state workgroup takes at
+                                  most 2)                                  */
     int32_t cols_per_wave;     /* headdim columns one wave computes          */
 } ssd_plan_info;
 

@@ -141,7 +141,17 @@ int make_plan(const ssd_dims* d, Plan* pl) {
             ssd::hw_supported(d->dtype, d->d_state, hg, npb)) {
             pl->K = K;
             pl->hw_npb = npb;
-            pl->hg_state = pl->hg_scan = hg;
+            // The state kernel groups at most two heads (four at d_state 128
+            // made it slower: 76 vs 62 us on the packed workload); span
+            // states are stored per head, so it need not match the scan.
+            pl->hg_scan = hg;
+            pl->hg_state = hg > 2 ? 2 : hg;
+            if (const char* e = getenv("SSD_HW_HEADS_STATE")) {
+                const int v = atoi(e);
+                if ((v == 1 || v == 2 || v == 4) && hpg % v == 0 &&
+                    ssd::hw_supported(d->dtype, d->d_state, v, npb))
+                    pl->hg_state = v;
+            }
         }
     }
     if (d->nseq > 0) {
