@@ -108,8 +108,8 @@ size_t ssd_fwd_workspace_bytes(const ssd_dims* dims);
  *               need separate workspaces.
  *   stream      hipStream_t to launch on (NULL = default stream)
  * S is b without cu_seqlens and nseq with them.  x, B, C and y must be
- * 16-byte aligned; they may be NULL only when b*L == 0.  Returns SSD_OK once
- * the work is queued on the stream.
+ * 16-byte aligned, d_raw aligned to its element size; they may be NULL only
+ * when b*L == 0.  Returns SSD_OK once the work is queued on the stream.
  */
 int ssd_fwd(const ssd_dims* dims,
             const void* x, const void* d_raw, float d_init,

@@ -372,6 +372,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
     const int64_t per_unit = 16 / esz;
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y)) return SSD_ERR_ALIGN;
+    if ((uintptr_t)d_raw % esz) return SSD_ERR_ALIGN;  // read one element per lane
     if (y_token_stride % per_unit != 0 || y_head_stride % per_unit != 0) return SSD_ERR_ALIGN;
     if (y_token_stride < 0 || y_head_stride < 0) return SSD_ERR_SHAPE;
     if (y_token_stride > ((int64_t)1 << 24)) return SSD_ERR_SHAPE;

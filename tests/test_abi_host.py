@@ -108,6 +108,7 @@ def test_rejects_bad_arguments(m):
     assert call(m, ok, reverse=2) == -2
     assert call(m, ok, x=FAKE + 8) == -4                               # ALIGN
     assert call(m, ok, y=FAKE + 2) == -4
+    assert call(m, ok, d_raw=FAKE + 1) == -4                           # d_raw: bf16 elements
     assert call(m, ok, yst=64 * 2 + 4) == -4
     assert call(m, ok, ws=None) == -6                                  # WORKSPACE
     assert call(m, ok, wsb=16) == -6
