@@ -1,0 +1,51 @@
+"""bench.py's host-side contract, without a GPU: the run refuses more than
+one GPU before touching any device, and the algorithmic byte counts behind
+the roofline fraction are the sums of the operands each stage must move,
+checked here against the layer workload's sizes worked out by hand
+(2 x 2048 tokens, 24 heads x headdim 64, d_state 128, bf16, 4-chunk spans,
+no initial state)."""
+import os
+import subprocess
+import sys
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from ssd_inputs import by_name  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+class _Plan:
+    def __init__(self, fused_pass, chunks_per_span=4):
+        self.fused_pass = fused_pass
+        self.chunks_per_span = chunks_per_span
+
+
+def test_layer_algorithmic_bytes_by_hand():
+    w = by_name("layer")
+    assert (w.tokens, w.nheads, w.headdim, w.d_state, w.ngroups, w.dtype) == \
+        (4096, 24, 64, 128, 1, "bf16")
+    spans = bench.spans_used(w, _Plan(1))
+    assert spans == 2 * (2048 // 64 // 4)  # 16 spans of 4 chunks
+    x = 4096 * 24 * 64 * 2          # x, and y the same size
+    d_raw = 4096 * 24 * 2
+    bc = 4096 * 1 * 128 * 2         # B, and C the same size
+    states = 16 * 24 * 128 * 64 * 2
+    decays = 16 * 24 * 4
+    final = 2 * 24 * 128 * 64 * 4
+    plan1 = bench.stage_bytes(w, _Plan(1), spans)
+    assert plan1["state"] == x + d_raw + bc + states + decays == 20121088
+    assert plan1["scan"] == x + d_raw + 2 * bc + states + decays + final + x == 35325440
+    plan0 = bench.stage_bytes(w, _Plan(0), spans)
+    assert plan0["pass"] == 2 * states + decays + final
+    assert plan0["scan"] == x + d_raw + 2 * bc + states + x
+    fused = bench.stage_bytes(w, _Plan(2), spans)["fused"]
+    assert fused == x + d_raw + 2 * bc + x + final + (16 - 2) * 24 * (128 * 64 * 2 + 4)
