@@ -76,6 +76,7 @@ SHAPES = [
     (1, 1, 2, 64, 128, 1),
     (1, 150, 2, 192, 64, 1),    # three column groups (the bidirectional workload's headdim)
     (1, 100, 4, 80, 128, 2),    # a partial second column group
+    (1, 257, 1, 512, 16, 1),    # the largest headdim: eight column groups
 ]
 
 
