@@ -47,7 +47,8 @@ enum {
     SSD_ERR_NULL_ARG = -1,        /* a required pointer is NULL                 */
     SSD_ERR_SHAPE = -2,           /* inconsistent or out-of-range sizes         */
     SSD_ERR_DTYPE = -3,           /* unknown dtype code                          */
-    SSD_ERR_ALIGN = -4,           /* pointer or stride not 16-byte aligned       */
+    SSD_ERR_ALIGN = -4,           /* pointer or stride misaligned (16 bytes;
+                                     d_raw / dd_raw: their element size)       */
     SSD_ERR_UNSUPPORTED = -5,     /* valid but not built (chunk_size, d_state..) */
     SSD_ERR_WORKSPACE = -6,       /* workspace NULL or smaller than required     */
     SSD_ERR_HIP = -7,             /* a HIP launch or runtime call failed         */
