@@ -161,3 +161,49 @@ def test_planted_bwd_mistakes_are_caught(kind, monkeypatch):
                     ("init_state", "dinit_state")]:
         worst = max(worst, F.rel_err(g[gk], _fd_grad(p, key, dy, dfin)))
     assert worst > 1e-3
+
+
+# ---------------------------------------------------------- the C adjoint oracle
+def _f32_problem(p, dy, dfin):
+    """Round every input to float32 (what the C oracle reads) so both
+    oracles see the same values."""
+    r = lambda a: None if a is None else np.asarray(a, np.float32).astype(np.float64)
+    q = {k: (r(v) if k not in ("d_init", "cu_seqlens") else v) for k, v in p.items()}
+    return q, r(dy), r(dfin)
+
+
+def _c_vs_numpy(p, dy, dfin, cu, rev, col_block):
+    from oracle import cref
+    g = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                      init_state=p["init_state"], d_final=dfin, cu_seqlens=cu, reverse=rev)
+    c = cref.ssd_ref_bwd_c(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                           init_state=p["init_state"], d_final=dfin, cu_seqlens=cu,
+                           reverse=rev, col_block=col_block)
+    for k in ("dx", "dd_raw", "dB", "dC", "dinit_state"):
+        assert F.rel_err(c[k], g[k]) <= 1e-12, k
+    assert abs(c["dd_init"] - g["dd_init"]) <= 1e-12 * max(1.0, float(np.abs(g["dd_raw"]).sum()))
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}")
+@pytest.mark.parametrize("col_block", [1, 2, 64])
+def test_c_bwd_matches_numpy_on_fd_cases(case, col_block):
+    """The C adjoint oracle equals the finite-difference-pinned numpy one
+    (to rounding) on the same cases, whatever its column split."""
+    seed, b, L, H, P, N, G, cu, rev = case
+    p, dy, dfin = _f32_problem(*_problem(seed, b, L, H, P, N, G, cu))
+    _c_vs_numpy(p, dy, dfin, cu, rev, col_block)
+
+
+@pytest.mark.parametrize("rev", [False, True])
+def test_c_bwd_long_walks_and_ragged_blocks(rev):
+    """Segments of several checkpoints (the walk recomputes states from
+    them), a ragged last column block, two B/C groups, and packed sequences
+    including an empty one and a one-token one."""
+    lens = [300, 0, 1, 77]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    p, dy, dfin = _f32_problem(*_problem(19, 1, int(cu[-1]), 4, 5, 3, 2, cu))
+    _c_vs_numpy(p, dy, dfin, cu, rev, col_block=2)
+    q, dq, fq = _f32_problem(*_problem(23, 2, 260, 2, 3, 4, 1))
+    _c_vs_numpy(q, dq, fq, None, rev, col_block=1)
+    q["init_state"] = None
+    _c_vs_numpy(q, dq, None, None, rev, col_block=3)
