@@ -24,10 +24,13 @@
  * flipped copy of any tensor is made.
  *
  * Ownership: the caller owns every buffer.  The library allocates no device
- * memory, does not synchronize the stream, and keeps no mutable global
- * state; calls on different streams with separate workspaces may run
- * concurrently.  All argument checks run on the host before any launch; on
- * an error status nothing is launched and no output is written.
+ * memory, does not synchronize the stream (except ssd_fwd / ssd_bwd with
+ * SSD_CHECK=1 in the environment, which copy cu_seqlens to the host to
+ * check it), and keeps no mutable global state; calls on different streams
+ * with separate workspaces may run concurrently.  All argument checks run
+ * on the host before any launch; on an error status nothing is launched and
+ * no output is written.  The library reads one environment variable,
+ * SSD_CHECK; its tuning choices are explicit arguments (ssd_tuning).
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -39,21 +42,25 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
     SSD_OK = 0,
     SSD_ERR_NULL_ARG = -1,        /* a required pointer is NULL                 */
-    SSD_ERR_SHAPE = -2,           /* inconsistent or out-of-range sizes         */
+    SSD_ERR_SHAPE = -2,           /* inconsistent or out-of-range sizes,
+                                     strides or tuning values                  */
     SSD_ERR_DTYPE = -3,           /* unknown dtype code                          */
     SSD_ERR_ALIGN = -4,           /* pointer or stride misaligned (16 bytes;
                                      d_raw / dd_raw: their element size)       */
     SSD_ERR_UNSUPPORTED = -5,     /* valid but not built (chunk_size, d_state..) */
     SSD_ERR_WORKSPACE = -6,       /* workspace NULL or smaller than required     */
     SSD_ERR_HIP = -7,             /* a HIP launch or runtime call failed         */
-    SSD_ERR_CU_SEQLENS = -8       /* cu_seqlens invalid (checked only when the
+    SSD_ERR_CU_SEQLENS = -8,      /* cu_seqlens invalid (checked only when the
                                      environment sets SSD_CHECK=1)               */
+    SSD_ERR_OVERLAP = -9          /* init_state and final_state (or d_final and
+                                     dinit_state) overlap without being the
+                                     same buffer                                */
 };
 
 /* Element type of x, d_raw, B, C and y.  States are always float32. */
@@ -73,61 +80,110 @@ typedef struct ssd_dims {
     int32_t dtype;       /* SSD_F32 or SSD_BF16                                */
 } ssd_dims;
 
+/*
+ * Element strides of the per-token tensors.  Token index k = bi * L + l
+ * runs over the flattened [b, L] tokens (so a batch row is L token strides
+ * further on); the innermost dimension is always contiguous.  Element
+ * (k, h, p) of x is at x + k * x_token + h * x_head + p, element (k, g, n)
+ * of B at B + k * B_token + g * B_group + n, and so on.  They let x, B, C
+ * and d_raw be views of one projection output, as in "Mamba-2架构与LaCT
+ * 并行计算技术解析" §1.1, where X, B, C and the raw step come from one
+ * linear map of the input.  Rules (checked on the host, SSD_ERR_ALIGN /
+ * SSD_ERR_SHAPE): every stride is >= 0 and at most 2^24; the strides of x,
+ * B, C, y and dy are multiples of 16 bytes; d_raw's are any element count.
+ * A NULL layout means every tensor is contiguous: x_token = H*P, x_head =
+ * P, d_raw_token = H, d_raw_head = 1, B_token = C_token = G*N, B_group =
+ * C_group = N, y and dy like x.
+ */
+typedef struct ssd_layout {
+    int64_t x_token, x_head;         /* x  [b, L, H, P]                       */
+    int64_t d_raw_token, d_raw_head; /* d_raw [b, L, H]                       */
+    int64_t B_token, B_group;        /* B  [b, L, G, N]                       */
+    int64_t C_token, C_group;        /* C  [b, L, G, N]                       */
+    int64_t y_token, y_head;         /* y  [b, L, H, P] (ssd_fwd's output,
+                                        ssd_bwd's input)                      */
+    int64_t dy_token, dy_head;       /* dy [b, L, H, P] (ssd_bwd only)        */
+} ssd_layout;
+
+/*
+ * Explicit choices that override the planner (timing sweeps and tests; the
+ * library reads no tuning from the environment).  Zero in every field means
+ * the planner's choice, so a zero-filled struct equals passing NULL.
+ * Values the sizes cannot take return SSD_ERR_SHAPE (SSD_ERR_UNSUPPORTED for
+ * shapes that are not built).
+ */
+typedef struct ssd_tuning {
+    int32_t kernel;           /* 1: span kernels; 2: head-wave kernels (bf16,
+                                 d_state 64 or 128)                           */
+    int32_t chunks_per_span;  /* 1..64 chunks walked by one workgroup         */
+    int32_t state_pass;       /* batch mode, span kernels: 1 state_pass launch
+                                 (plan 0); 2 folded into the scan (plan 1);
+                                 3 one fused launch (plan 2)                  */
+    int32_t heads_state;      /* heads per state workgroup: 1, 2 (head-wave: 4)*/
+    int32_t heads_scan;       /* heads per scan workgroup: 1, 2 (head-wave: 4) */
+    int32_t cols_per_wave;    /* head-wave kernels: 32, or 64 at d_state 64    */
+    int32_t bwd_heads;        /* heads per backward gradient workgroup        */
+    int32_t bwd_state_chunks; /* chunks per backward chunk-state workgroup: 1, 4 */
+    int32_t state_f32;        /* 1: span states stored in float32 for bf16
+                                 inputs (span kernels, plans 0 and 1)        */
+    int32_t reserved[7];      /* must be 0                                    */
+} ssd_tuning;
+
 /* ABI version of the loaded library (SSD_ABI_VERSION it was built with). */
 int ssd_abi_version(void);
 
-/* Bytes of device workspace ssd_fwd needs for these sizes (0 when the sizes
- * are invalid).  The value depends only on *dims, never on data. */
+/* Bytes of device workspace ssd_fwd needs for these sizes with the
+ * planner's choices (0 when the sizes are invalid).  A pure function of
+ * *dims: never of data or the environment. */
 size_t ssd_fwd_workspace_bytes(const ssd_dims* dims);
 
 /*
- * Forward scan.  Device pointers, all row-major and contiguous except y:
+ * Forward scan.  Device pointers:
  *   x           [b, L, H, P]   dtype
  *   d_raw       [b, L, H]      dtype
  *   d_init      scalar added to d_raw before softplus
  *   B, C        [b, L, G, N]   dtype
- *   init_state  [S, H, N, P]   float32, or NULL for zeros
+ *   init_state  [S, H, N, P]   float32 contiguous, or NULL for zeros
  *   cu_seqlens  [nseq + 1]     int32 on the device, or NULL; must start at 0,
  *               be non-decreasing and end at L (only checked when SSD_CHECK=1;
  *               other values are clamped into range so no access leaves the
  *               buffers, but the result is then unspecified)
  *   reverse     0 = causal, 1 = anti-causal within each sequence
- *   y           output [b, L, H, P] of dtype, element (bi, l, h, p) at
- *               y + (bi*L + l)*y_token_stride + h*y_head_stride + p;
- *               strides in elements, multiples of 16 bytes; the token
- *               stride at most 2^24
- *   final_state output [S, H, N, P] float32, or NULL to skip
+ *   y           output [b, L, H, P] of dtype
+ *   final_state output [S, H, N, P] float32 contiguous, or NULL to skip; it
+ *               may be the same buffer as init_state (an in-place state
+ *               update between calls), but not overlap it otherwise
+ *               (SSD_ERR_OVERLAP)
+ *   layout      strides of x, d_raw, B, C and y (see ssd_layout), or NULL
  *   workspace   device scratch of at least ssd_fwd_workspace_bytes(dims)
- *               bytes, 256-byte aligned.  Zero-fill it once before its
- *               first use; after that leave it alone between calls (each
- *               call leaves it ready for the next, whatever its sizes).
- *               Its first 256 bytes are a header of 32-bit words: word 0
- *               counts the fused launches, word 1 is their ticket counter
- *               (0 between calls), word 2 counts flag waits that ran out
- *               (stays 0 unless the header was not zero-filled; the results
- *               of such a call are unspecified).  Calls that overlap in time
- *               need separate workspaces.
+ *               bytes, 256-byte aligned.  It needs no initialization and
+ *               holds nothing the caller reads; calls that overlap in time
+ *               need separate workspaces.  Its first 256 bytes are a header
+ *               of 32-bit words: word 2 counts the bounded flag waits of the
+ *               last fused launch that ran out (it stays 0).
  *   stream      hipStream_t to launch on (NULL = default stream)
  * S is b without cu_seqlens and nseq with them.  x, B, C and y must be
  * 16-byte aligned, d_raw aligned to its element size; they may be NULL only
- * when b*L == 0.  Returns SSD_OK once the work is queued on the stream.
+ * when b*L == 0.  y must not overlap the inputs.  Returns SSD_OK once the
+ * work is queued on the stream.
  */
-int ssd_fwd(const ssd_dims* dims,
+int ssd_fwd(const ssd_dims* dims, const ssd_layout* layout,
             const void* x, const void* d_raw, float d_init,
             const void* B, const void* C,
             const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
-            void* y, int64_t y_token_stride, int64_t y_head_stride,
-            float* final_state,
+            void* y, float* final_state,
             void* workspace, size_t workspace_bytes,
             void* stream);
 
-/* How ssd_fwd splits a problem of these sizes (a pure function of *dims). */
+/* How ssd_fwd / ssd_bwd split a problem of these sizes (a pure function of
+ * *dims and *tuning). */
 typedef struct ssd_plan_info {
     int32_t chunks_per_span;   /* 64-token chunks walked by one workgroup; the
                                   state stays on chip inside a span          */
     int32_t col_groups;        /* headdim columns are split in groups of 64  */
     int64_t nspan;             /* span slots (upper bound with cu_seqlens)   */
-    uint64_t workspace_bytes;  /* = ssd_fwd_workspace_bytes(dims)            */
+    uint64_t workspace_bytes;  /* workspace ssd_fwd_ex needs with this tuning
+                                  (= ssd_fwd_workspace_bytes(dims) for NULL) */
     int32_t fused_pass;        /* 0: stages STATE, PASS and SCAN launch one
                                   kernel each.  1: SCAN forms every span's
                                   incoming state from the span states itself
@@ -135,23 +191,30 @@ typedef struct ssd_plan_info {
                                   launch that does STATE, PASS and SCAN
                                   (their workgroups hand span states to each
                                   other); STATE and PASS launch nothing.
-                                  1 is the default in batch mode with 1..8
-                                  spans per sequence, else 0; the environment
-                                  variable SSD_FUSE_PASS=0/1/2 forces one.
-                                  Always 0 with head-wave kernels.          */
+                                  The planner takes 1 in batch mode with
+                                  1..8 spans per sequence, else 0; always 0
+                                  with head-wave kernels, and whenever
+                                  final_state is init_state.               */
     int32_t head_wave;         /* 1: head-wave kernels (one wave computes every
                                   product of one head for cols_per_wave
                                   headdim columns); 0: span kernels (four
                                   waves per head, 16 columns each)          */
     int32_t heads_per_wg;      /* heads sharing one scan workgroup's B / C
-                                  tiles (a head-wave state workgroup takes at
-                                  most 2)                                  */
+                                  tiles                                     */
     int32_t cols_per_wave;     /* headdim columns one wave computes          */
+    int32_t heads_per_state_wg;/* heads of one state workgroup               */
+    int32_t state_bytes;       /* bytes of one stored span-state entry       */
+    uint64_t bwd_workspace_bytes; /* workspace ssd_bwd_ex needs (0: the
+                                  backward is not built for these sizes)     */
+    int32_t bwd_heads_per_wg;  /* heads of one backward gradient workgroup   */
+    int32_t bwd_head_subsets;  /* dB / dC partials added after it            */
+    int32_t bwd_state_chunks;  /* chunks of one backward chunk-state workgroup */
+    int32_t reserved;
 } ssd_plan_info;
 
-/* Fills *out for these sizes; returns the status ssd_fwd's size checks
- * would give. */
-int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out);
+/* Fills *out for these sizes and tuning (NULL = the planner's choices);
+ * returns the status ssd_fwd_ex's size and tuning checks would give. */
+int ssd_fwd_plan(const ssd_dims* dims, const ssd_tuning* tuning, ssd_plan_info* out);
 
 /* Stages of ssd_fwd, one kernel launch each, in this order. */
 enum {
@@ -164,18 +227,20 @@ enum {
     SSD_STAGE_ALL = 15
 };
 
-/* ssd_fwd restricted to the stages in stage_mask, for callers that time or
- * interleave work between stages.  Same arguments and checks as ssd_fwd;
- * running the stages in the order above on one stream with one workspace
- * (left untouched in between) gives exactly ssd_fwd's result. */
-int ssd_fwd_stages(uint32_t stage_mask, const ssd_dims* dims,
-                   const void* x, const void* d_raw, float d_init,
-                   const void* B, const void* C,
-                   const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
-                   void* y, int64_t y_token_stride, int64_t y_head_stride,
-                   float* final_state,
-                   void* workspace, size_t workspace_bytes,
-                   void* stream);
+/* ssd_fwd with explicit tuning (NULL = the planner's choices; the workspace
+ * is then ssd_fwd_plan's workspace_bytes for that tuning) and restricted to
+ * the stages in stage_mask, for callers that time or interleave work
+ * between stages.  Running the stages in the order above on one stream with
+ * one workspace (left untouched in between) and the same tuning gives
+ * exactly ssd_fwd_ex's result with SSD_STAGE_ALL. */
+int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuning,
+               const ssd_layout* layout,
+               const void* x, const void* d_raw, float d_init,
+               const void* B, const void* C,
+               const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+               void* y, float* final_state,
+               void* workspace, size_t workspace_bytes,
+               void* stream);
 
 /*
  * Backward pass: the gradients of a loss L with respect to every input of
@@ -197,36 +262,47 @@ int ssd_fwd_stages(uint32_t stage_mask, const ssd_dims* dims,
  *
  * Arguments as ssd_fwd, plus:
  *   y           the forward output of these inputs (as ssd_fwd wrote it),
- *               strided like ssd_fwd's y
- *   dy          dL/dy, dtype, the same layout rules as y (its own strides)
+ *               strides layout->y_*
+ *   dy          dL/dy, dtype, strides layout->dy_*
  *   d_final     dL/d final_state [S, H, N, P] float32, or NULL for zeros
- *   dx          output [b, L, H, P] dtype, contiguous
- *   dd_raw      output [b, L, H] dtype
- *   dB, dC      output [b, L, G, N] dtype
+ *   dx          output, dtype, laid out like x (strides layout->x_*)
+ *   dd_raw      output, dtype, laid out like d_raw
+ *   dB, dC      outputs, dtype, laid out like B and C
  *   dinit_state output [S, H, N, P] float32 (the gradient at the given
- *               init_state, or at zeros when it is NULL), or NULL to skip
+ *               init_state, or at zeros when it is NULL), or NULL to skip;
+ *               it may be the same buffer as d_final, but not overlap it
+ *               otherwise (SSD_ERR_OVERLAP)
  *   dd_init     output: one float32 on the device, or NULL to skip
  *   workspace   at least ssd_bwd_workspace_bytes(dims) bytes, 256-byte
- *               aligned (every call overwrites what it reads; no zero-fill
- *               needed); calls that overlap in time need separate workspaces
- * x, B, C, y, dy, dx, dB and dC must be 16-byte aligned; strides are in
- * elements, multiples of 16 bytes, at most 2^24.  Outputs for tokens outside
- * every cu_seqlens segment are not written.  Returns SSD_OK once the work
- * is queued on the stream.
+ *               aligned, no initialization needed; calls that overlap in
+ *               time need separate workspaces
+ * x, B, C, y, dy, dx, dB and dC must be 16-byte aligned.  The gradients must
+ * not overlap the inputs.  Outputs for tokens outside every cu_seqlens
+ * segment are not written.  Returns SSD_OK once the work is queued.
  */
 size_t ssd_bwd_workspace_bytes(const ssd_dims* dims);
 
-int ssd_bwd(const ssd_dims* dims,
+int ssd_bwd(const ssd_dims* dims, const ssd_layout* layout,
             const void* x, const void* d_raw, float d_init,
             const void* B, const void* C,
             const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
-            const void* y, int64_t y_token_stride, int64_t y_head_stride,
-            const void* dy, int64_t dy_token_stride, int64_t dy_head_stride,
-            const float* d_final,
+            const void* y, const void* dy, const float* d_final,
             void* dx, void* dd_raw, void* dB, void* dC,
             float* dinit_state, float* dd_init,
             void* workspace, size_t workspace_bytes,
             void* stream);
+
+/* ssd_bwd with explicit tuning (NULL = the planner's choices; the workspace
+ * is then ssd_fwd_plan's bwd_workspace_bytes for that tuning). */
+int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout* layout,
+               const void* x, const void* d_raw, float d_init,
+               const void* B, const void* C,
+               const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+               const void* y, const void* dy, const float* d_final,
+               void* dx, void* dd_raw, void* dB, void* dC,
+               float* dinit_state, float* dd_init,
+               void* workspace, size_t workspace_bytes,
+               void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);

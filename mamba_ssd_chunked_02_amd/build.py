@@ -28,18 +28,40 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every source to an object in parallel (one hipcc each), then
+    link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+        return r.returncode, err
+
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *compile_flags, *extra, *inc, "-c", "-o", obj,
+                     os.path.join(CSRC, src)])
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(run, cmds))
+    for (rc, err), cmd in zip(results, cmds):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) on {cmd[-1]}:\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    rc, err = run([HIPCC, *FLAGS, *extra, "-o", tmp, *objs])
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB)
     return LIB
 

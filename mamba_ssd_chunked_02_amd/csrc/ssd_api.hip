@@ -19,12 +19,6 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// An integer from the environment (tuning overrides), or dflt.
-int getenv_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e && e[0] ? atoi(e) : dflt;
-}
-
 struct Plan {
     int32_t K = 1;          // chunks per span
     int32_t sps = 0;        // spans per sequence (batch mode)
@@ -35,23 +29,21 @@ struct Plan {
                             // launch); 2: one fused launch does every stage
     int32_t hw_npb = 0;     // head-wave kernels: 16-column blocks per wave;
                             // 0 = span kernels
+    int32_t state_f32 = 0;  // span states stored in float32
     int64_t nspan = 0;      // span slots
+    int64_t nsync = 0;      // 32-bit words the fused launch resets (plan 2)
     size_t off_sync = 0, off_states = 0, off_decay = 0, off_cu = 0, off_spoff = 0, off_table = 0;
     size_t total = 0;
 };
 
+const ssd_tuning kNoTuning = {};
+
 // Chunks per span: the state stays on chip inside a span and only span
 // borders go through HBM, so longer spans move fewer bytes; but each span is
-// walked by one workgroup, so spans stay short enough that the span_scan grid
-// keeps >= 4096 workgroups (16 per CU) once past four chunks.
-// SSD_SPAN_CHUNKS overrides it (tuning sweeps).
+// walked by one workgroup, so spans stay short enough to keep the grid wide.
+// Four-chunk spans, or eight when that still leaves >= 2048 span x
+// head-group items (8192 tokens x 80 heads: 8-chunk spans run 15 % faster).
 int32_t choose_k(int64_t nch, int64_t groups) {
-    if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
-        const int v = atoi(e);
-        if (v >= 1 && v <= 64) return v;
-    }
-    // Four-chunk spans, or eight when that still leaves >= 1024 span x
-    // head-group items (the wide workload: 8-chunk spans run 15 % faster)
     int32_t K = 4;
     while (K < 8 && ceil_div(nch, K) * groups >= 2048) K *= 2;
     return K;
@@ -60,57 +52,32 @@ int32_t choose_k(int64_t nch, int64_t groups) {
 // Head-wave kernels (bf16, d_state 64 / 128): a head's work for a chunk in
 // one wave per 32 headdim columns (npb 2) or 64 (npb 4, d_state 64 only).
 // Their per-chunk pipeline is cheaper than the span kernels' but needs long
-// spans to pay for the state pass, so they serve problems with at least
-// 16384 chunk-head-column-group work items (on one MI355X the span kernels
-// are faster below that: 119 vs 146 us on 8192 tokens x 80 heads).  Spans: the longest of 32, 16, ... chunks that
-// still give >= 2048 waves; 4 heads per workgroup at d_state 128 (they share
-// the B / C tiles and the causal C B^T), 2 at d_state 64.
-// SSD_KERNEL=span|hw forces a family; SSD_HW_NPB, SSD_HW_HEADS and
-// SSD_SPAN_CHUNKS override the shape (tuning sweeps).
-bool choose_hw(int64_t nch, int64_t heads, int64_t npg, int32_t hpg, int32_t N, int32_t* K,
-               int32_t* npb, int32_t* hg) {
-    const char* kf = getenv("SSD_KERNEL");
-    if (kf && strcmp(kf, "span") == 0) return false;
-    const bool forced = kf && strcmp(kf, "hw") == 0;
-    if (!forced && nch * heads * npg < 16384) return false;
-    int32_t b = 2;
+// spans to pay for the state pass, so the planner takes them for problems
+// with at least 16384 chunk-head-column-group work items (on one MI355X the
+// span kernels are faster below that: 119 vs 146 us on 8192 tokens x 80
+// heads).  Spans: the longest of 32, 16, ... chunks that still give >= 2048
+// waves; 4 heads per workgroup at d_state 128 (they share the B / C tiles
+// and the causal C B^T), 2 at d_state 64.
+bool choose_hw(const ssd_tuning& t, int64_t nch, int64_t heads, int64_t npg, int32_t hpg,
+               int32_t N, int32_t* K, int32_t* npb, int32_t* hg) {
+    if (t.kernel == 1) return false;
+    if (t.kernel != 2 && nch * heads * npg < 16384) return false;
+    int32_t b = t.cols_per_wave ? t.cols_per_wave / 16 : 2;
     auto waves = [&](int32_t k) { return ceil_div(nch, k) * heads * npg * (4 / b); };
     int32_t k = 32;
     while (k > 1 && waves(k) < 2048) k /= 2;
     int32_t g = N >= 128 ? 4 : 2;
     while (hpg % g) g /= 2;
-    if (const char* e = getenv("SSD_HW_NPB")) {
-        const int v = atoi(e);
-        if (v == 2 || (v == 4 && N <= 64)) b = v;
-    }
-    if (const char* e = getenv("SSD_HW_HEADS")) {
-        const int v = atoi(e);
-        if ((v == 1 || v == 2 || v == 4) && hpg % v == 0) g = v;
-    }
-    if (const char* e = getenv("SSD_SPAN_CHUNKS")) {
-        const int v = atoi(e);
-        if (v >= 1 && v <= 64) k = v;
-    }
-    *K = k;
+    if (t.heads_scan) g = t.heads_scan;
+    *K = t.chunks_per_span ? t.chunks_per_span : k;
     *npb = b;
     *hg = g;
     return true;
 }
 
-// Heads per workgroup: `dflt` unless the named environment variable asks
-// for 1 or 2 up to `most` (tuning sweeps).  Both span kernels run one head
-// per workgroup by default: more, smaller workgroups overlap their load,
-// compute and store phases better than wider ones sharing B and C.
-int32_t heads_override(const char* name, int32_t dflt, int32_t most) {
-    if (const char* e = getenv(name)) {
-        const int v = atoi(e);
-        if ((v == 1 || v == 2) && v <= most) return v;
-    }
-    return dflt < most ? dflt : most;
-}
-
-int make_plan(const ssd_dims* d, Plan* pl) {
+int make_plan(const ssd_dims* d, const ssd_tuning* tun, Plan* pl) {
     if (!d) return SSD_ERR_NULL_ARG;
+    const ssd_tuning& t = tun ? *tun : kNoTuning;
     if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_DTYPE;
     if (d->batch < 1 || d->seqlen < 0 || d->nheads < 1 || d->ngroups < 1 || d->nseq < 0)
         return SSD_ERR_SHAPE;
@@ -123,40 +90,68 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     const int64_t T = (int64_t)d->batch * d->seqlen;
     if (d->nseq > 0 && T > INT32_MAX) return SSD_ERR_SHAPE;
     if (T > ((int64_t)1 << 40)) return SSD_ERR_SHAPE;
+    // tuning values in range
+    for (int32_t r : t.reserved)
+        if (r) return SSD_ERR_SHAPE;
+    if (t.kernel < 0 || t.kernel > 2 || t.chunks_per_span < 0 || t.chunks_per_span > 64 ||
+        t.state_pass < 0 || t.state_pass > 3 || t.heads_state < 0 || t.heads_scan < 0 ||
+        (t.cols_per_wave != 0 && t.cols_per_wave != 32 && t.cols_per_wave != 64) ||
+        t.bwd_heads < 0 || (t.bwd_state_chunks != 0 && t.bwd_state_chunks != 1 &&
+                            t.bwd_state_chunks != 4) ||
+        t.state_f32 < 0 || t.state_f32 > 1)
+        return SSD_ERR_SHAPE;
+    const int32_t hpg = d->nheads / d->ngroups;
+    if (t.bwd_heads && (hpg % t.bwd_heads || t.bwd_heads > ssd::kBwdMaxHeads)) return SSD_ERR_SHAPE;
+    const bool hw_ok = d->dtype == SSD_BF16 && (d->d_state == 64 || d->d_state == 128);
+    if (t.kernel == 2 && !hw_ok) return SSD_ERR_UNSUPPORTED;
+    if (t.kernel == 2 && t.state_f32) return SSD_ERR_SHAPE;
+    if (t.cols_per_wave == 64 && !(hw_ok && d->d_state == 64)) return SSD_ERR_SHAPE;
 
     pl->npg = (int32_t)ceil_div(d->headdim, kPGroup);
-    // heads per workgroup: as many as the kernel carries, all in one B/C group
-    const int32_t hpg = d->nheads / d->ngroups;
-    pl->hg_state = heads_override("SSD_HEADS_STATE", 1, ssd::span_max_heads(d->dtype, d->d_state, false));
-    while (hpg % pl->hg_state) pl->hg_state /= 2;
-    pl->hg_scan = heads_override("SSD_HEADS_SCAN", 1, ssd::span_max_heads(d->dtype, d->d_state, true));
-    while (hpg % pl->hg_scan) pl->hg_scan /= 2;
+    pl->state_f32 = t.state_f32;
+    // Span kernels carry one head per workgroup by default: more, smaller
+    // workgroups overlap their load, compute and store phases better than
+    // wider ones sharing B and C.
+    const int32_t hs_max = ssd::span_max_heads(d->dtype, d->d_state, false);
+    const int32_t hc_max = ssd::span_max_heads(d->dtype, d->d_state, true);
+    pl->hg_state = t.heads_state ? t.heads_state : 1;
+    pl->hg_scan = t.heads_scan ? t.heads_scan : 1;
     const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
                                           : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);
-    pl->K = choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg);
+    pl->K = t.chunks_per_span ? t.chunks_per_span
+                              : choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg);
     // Large bf16 problems with d_state 64 or 128 run the head-wave kernels.
-    if (d->dtype == SSD_BF16 && (d->d_state == 64 || d->d_state == 128)) {
+    bool hw = false;
+    if (hw_ok && !t.state_f32) {
         int32_t K, npb, hg;
-        if (choose_hw(nch_bound, d->nheads, pl->npg, hpg, d->d_state, &K, &npb, &hg) &&
-            ssd::hw_supported(d->dtype, d->d_state, hg, npb)) {
-            pl->K = K;
-            pl->hw_npb = npb;
+        if (choose_hw(t, nch_bound, d->nheads, pl->npg, hpg, d->d_state, &K, &npb, &hg)) {
             // The state kernel groups at most two heads (four at d_state 128
             // made it slower: 76 vs 62 us on the packed workload); span
             // states are stored per head, so it need not match the scan.
-            pl->hg_scan = hg;
-            pl->hg_state = hg > 2 ? 2 : hg;
-            if (const char* e = getenv("SSD_HW_HEADS_STATE")) {
-                const int v = atoi(e);
-                if ((v == 1 || v == 2 || v == 4) && hpg % v == 0 &&
-                    ssd::hw_supported(d->dtype, d->d_state, v, npb))
-                    pl->hg_state = v;
+            const int32_t hs = t.heads_state ? t.heads_state : (hg > 2 ? 2 : hg);
+            hw = ssd::hw_supported(d->dtype, d->d_state, hg, npb) && hpg % hg == 0 &&
+                 ssd::hw_supported(d->dtype, d->d_state, hs, npb) && hpg % hs == 0;
+            // a shape asked for explicitly must exist; the planner's own
+            // choice falls back to the span kernels
+            if (!hw && (t.kernel == 2 || t.cols_per_wave)) return SSD_ERR_SHAPE;
+            if (hw) {
+                pl->K = K;
+                pl->hw_npb = npb;
+                pl->hg_scan = hg;
+                pl->hg_state = hs;
             }
         }
+    }
+    if (!hw) {
+        if (pl->hg_state > hs_max || pl->hg_scan > hc_max || pl->hg_state > 2 || pl->hg_scan > 2 ||
+            hpg % pl->hg_state || hpg % pl->hg_scan)
+            return SSD_ERR_SHAPE;
+        if (t.cols_per_wave) return SSD_ERR_SHAPE;
     }
     if (d->nseq > 0) {
         pl->sps = 0;
         pl->nspan = ceil_div(T, (int64_t)kChunk * pl->K) + d->nseq;
+        if (t.state_pass) return SSD_ERR_SHAPE;  // packed batches always take plan 0
     } else {
         pl->sps = (int32_t)ceil_div(ceil_div(d->seqlen, kChunk), pl->K);
         pl->nspan = (int64_t)d->batch * pl->sps;
@@ -164,17 +159,19 @@ int make_plan(const ssd_dims* d, Plan* pl) {
         // states of its sequence itself, which saves the state_pass launch
         // (with 16 the fold's re-reads cost more than the launch).  Empty
         // sequences keep the three launches (state_pass copies init_state to
-        // final_state).  SSD_FUSE_PASS=0 / 1 / 2 forces the three launches,
-        // these two, or one fused launch whose workgroups hand the span
-        // states to the later spans of their sequence (as fast as the two
-        // launches at the sizes measured, so not the default).
-        const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
+        // final_state).  Plan 2, one fused launch whose workgroups hand the
+        // span states to the later spans of their sequence, is as fast as
+        // plan 1 at the sizes measured, so only taken when asked for.
         pl->fuse = pl->sps > 0 && pl->sps <= 8 ? 1 : 0;
-        if (const char* e = getenv("SSD_FUSE_PASS")) {
-            if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) pl->fuse = e[0] - '0';
+        if (t.state_pass) {
+            if (hw && t.state_pass != 1) return SSD_ERR_SHAPE;  // head-wave: three launches
+            if (pl->sps == 0 && t.state_pass != 1) return SSD_ERR_SHAPE;
+            pl->fuse = t.state_pass - 1;
         }
-        if (pl->sps == 0 || pl->hw_npb) pl->fuse = 0;  // head-wave: three launches
-        if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) pl->fuse = 1;
+        if (hw) pl->fuse = 0;
+        if (pl->state_f32 && pl->fuse == 2) return SSD_ERR_SHAPE;
+        const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
+        if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
     }
     // The span kernels decode their work items in 32 bits.
     if (pl->nspan * d->nheads * pl->npg >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
@@ -186,11 +183,13 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     off = align_up(off + ssd::kSyncHeader * sizeof(uint32_t));
     if (pl->fuse == 2) {
         const int64_t chains = (int64_t)d->batch * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
-        off = align_up(off + (size_t)chains * sizeof(uint64_t) +
-                       (size_t)pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg * sizeof(uint32_t));
+        const int64_t words = 2 * chains + pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
+        pl->nsync = ssd::kSyncHeader + words;
+        off = align_up(off + (size_t)words * sizeof(uint32_t));
     }
     pl->off_states = off;
-    const size_t esz = d->dtype == SSD_BF16 ? 2 : 4;  // span states use the input type
+    // span states: the input type, or float32 when asked for
+    const size_t esz = (d->dtype == SSD_BF16 && !pl->state_f32) ? 2 : 4;
     off = align_up(off + (size_t)pl->nspan * d->nheads * d->headdim * d->d_state * esz);
     pl->off_decay = off;
     off = align_up(off + (size_t)pl->nspan * d->nheads * sizeof(float));
@@ -206,6 +205,46 @@ int make_plan(const ssd_dims* d, Plan* pl) {
     return SSD_OK;
 }
 
+// Strides of every per-token tensor (elements): the caller's layout, or the
+// contiguous one.
+ssd_layout resolve_layout(const ssd_dims& d, const ssd_layout* lay) {
+    if (lay) return *lay;
+    ssd_layout l;
+    l.x_token = l.y_token = l.dy_token = (int64_t)d.nheads * d.headdim;
+    l.x_head = l.y_head = l.dy_head = d.headdim;
+    l.d_raw_token = d.nheads;
+    l.d_raw_head = 1;
+    l.B_token = l.C_token = (int64_t)d.ngroups * d.d_state;
+    l.B_group = l.C_group = d.d_state;
+    return l;
+}
+
+// Stride rules: >= 0 and <= 2^24 elements; the 16-byte-row tensors' strides
+// a multiple of 16 bytes.  bwd also checks dy's.
+int check_layout(const ssd_dims& d, const ssd_layout& l, bool bwd) {
+    const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
+    const int64_t per_unit = 16 / esz;
+    const int64_t lim = (int64_t)1 << 24;
+    const int64_t all[] = {l.x_token, l.x_head, l.d_raw_token, l.d_raw_head, l.B_token, l.B_group,
+                           l.C_token, l.C_group, l.y_token, l.y_head, l.dy_token, l.dy_head};
+    for (int i = 0; i < (bwd ? 12 : 10); ++i)
+        if (all[i] < 0 || all[i] > lim) return SSD_ERR_SHAPE;
+    const int64_t rows[] = {l.x_token, l.x_head, l.B_token, l.B_group, l.C_token, l.C_group,
+                            l.y_token, l.y_head, l.dy_token, l.dy_head};
+    for (int i = 0; i < (bwd ? 10 : 8); ++i)
+        if (rows[i] % per_unit) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+// Two [S, H, N, P] float32 state buffers: 0 when disjoint (or either is
+// NULL), 1 when they are the same buffer, -1 when they partly overlap.
+int state_alias(const void* a, const void* b, size_t bytes) {
+    if (!a || !b || bytes == 0) return 0;
+    if (a == b) return 1;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return (x < y + bytes && y < x + bytes) ? -1 : 0;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Backward plan.  Every chunk is its own span, so the two state passes
@@ -214,22 +253,23 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // workspace; the gradient kernel then treats the chunks independently.  Its
 // workgroups take hs heads of one B/C group; hs is the largest divisor of
 // the group's heads that still gives >= 256 workgroups, one per CU (the
-// kernel's LDS allows one; SSD_BWD_HEADS overrides it), and the head
-// subsets' dB / dC partials are added after it.
+// kernel's LDS allows one; ssd_tuning.bwd_heads overrides it), and the
+// head subsets' dB / dC partials are added after it.
 struct BPlan {
     int64_t nchunk = 0;    // chunk slots
     int32_t cps = 0;       // chunks per sequence (batch mode)
     int32_t nsub = 1, hs = 1;
     size_t off_cu = 0, off_spoff = 0, off_table = 0;
+    int32_t state_chunks = 4;  // chunks walked by one chunk-state workgroup
     int64_t nspan4 = 0;    // (varlen) four-chunk span slots of the chunk-state pass
     size_t off_cu4 = 0, off_spoff4 = 0, off_table4 = 0;
     size_t off_sa = 0, off_da = 0, off_sb = 0, off_db = 0;
     size_t off_pb = 0, off_pc = 0, off_pi = 0, total = 0;
 };
 
-int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
+int make_bwd_plan(const ssd_dims* d, const ssd_tuning* tun, BPlan* bp) {
     Plan pl;
-    const int st = make_plan(d, &pl);  // the forward's size checks
+    const int st = make_plan(d, tun, &pl);  // the forward's size and tuning checks
     if (st != SSD_OK) return st;
     if (!ssd::bwd_supported(d->dtype, d->d_state)) return SSD_ERR_UNSUPPORTED;
     const int64_t T = (int64_t)d->batch * d->seqlen;
@@ -243,10 +283,8 @@ int make_bwd_plan(const ssd_dims* d, BPlan* bp) {
             break;
         }
     }
-    if (const char* e = getenv("SSD_BWD_HEADS")) {
-        const int v = atoi(e);
-        if (v >= 1 && v <= hpg && v <= ssd::kBwdMaxHeads && hpg % v == 0) hs = v;
-    }
+    if (tun && tun->bwd_heads) hs = tun->bwd_heads;  // checked by make_plan
+    if (tun && tun->bwd_state_chunks) bp->state_chunks = tun->bwd_state_chunks;
     bp->hs = hs;
     bp->nsub = hpg / hs;
     const size_t esz = d->dtype == SSD_BF16 ? 2 : 4;
@@ -308,7 +346,7 @@ int ssd_abi_version(void) { return SSD_ABI_VERSION; }
 
 size_t ssd_fwd_workspace_bytes(const ssd_dims* dims) {
     Plan pl;
-    if (make_plan(dims, &pl) != SSD_OK) return 0;
+    if (make_plan(dims, nullptr, &pl) != SSD_OK) return 0;
     return pl.total;
 }
 
@@ -316,7 +354,8 @@ const char* ssd_status_string(int status) {
     switch (status) {
         case SSD_OK: return "SSD_OK: success";
         case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG: a required pointer is NULL";
-        case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: inconsistent or out-of-range sizes or strides";
+        case SSD_ERR_SHAPE:
+            return "SSD_ERR_SHAPE: inconsistent or out-of-range sizes, strides or tuning values";
         case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype code";
         case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer or stride not 16-byte aligned";
         case SSD_ERR_UNSUPPORTED:
@@ -325,43 +364,54 @@ const char* ssd_status_string(int status) {
         case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP runtime call or kernel launch failed";
         case SSD_ERR_CU_SEQLENS:
             return "SSD_ERR_CU_SEQLENS: cu_seqlens not 0..L and non-decreasing";
+        case SSD_ERR_OVERLAP:
+            return "SSD_ERR_OVERLAP: state buffers overlap without being the same buffer";
     }
     return "unknown ssd status";
 }
 
-int ssd_fwd_plan(const ssd_dims* dims, ssd_plan_info* out) {
+int ssd_fwd_plan(const ssd_dims* dims, const ssd_tuning* tuning, ssd_plan_info* out) {
     Plan pl;
-    const int st = make_plan(dims, &pl);
+    const int st = make_plan(dims, tuning, &pl);
     if (st != SSD_OK) return st;
     if (!out) return SSD_ERR_NULL_ARG;
+    memset(out, 0, sizeof(*out));
     out->chunks_per_span = pl.K;
     out->col_groups = pl.npg;
     out->nspan = pl.nspan;
     out->workspace_bytes = pl.total;
     out->fused_pass = pl.fuse;
     out->heads_per_wg = pl.hg_scan;
+    out->heads_per_state_wg = pl.hg_state;
     out->cols_per_wave = pl.hw_npb ? 16 * pl.hw_npb : 16;
     out->head_wave = pl.hw_npb ? 1 : 0;
+    out->state_bytes = (dims->dtype == SSD_BF16 && !pl.state_f32) ? 2 : 4;
+    BPlan bp;
+    if (make_bwd_plan(dims, tuning, &bp) == SSD_OK) {
+        out->bwd_workspace_bytes = bp.total;
+        out->bwd_heads_per_wg = bp.hs;
+        out->bwd_head_subsets = bp.nsub;
+        out->bwd_state_chunks = bp.state_chunks;
+    }
     return SSD_OK;
 }
 
-int ssd_fwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init, const void* B,
-            const void* C, const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
-            void* y, int64_t y_token_stride, int64_t y_head_stride, float* final_state,
+int ssd_fwd(const ssd_dims* dims, const ssd_layout* layout, const void* x, const void* d_raw,
+            float d_init, const void* B, const void* C, const float* init_state,
+            const int32_t* cu_seqlens, int32_t reverse, void* y, float* final_state,
             void* workspace, size_t workspace_bytes, void* stream) {
-    return ssd_fwd_stages(SSD_STAGE_ALL, dims, x, d_raw, d_init, B, C, init_state, cu_seqlens,
-                          reverse, y, y_token_stride, y_head_stride, final_state, workspace,
-                          workspace_bytes, stream);
+    return ssd_fwd_ex(SSD_STAGE_ALL, dims, nullptr, layout, x, d_raw, d_init, B, C, init_state,
+                      cu_seqlens, reverse, y, final_state, workspace, workspace_bytes, stream);
 }
 
-int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const void* d_raw,
-                   float d_init, const void* B, const void* C, const float* init_state,
-                   const int32_t* cu_seqlens, int32_t reverse, void* y, int64_t y_token_stride,
-                   int64_t y_head_stride, float* final_state, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
+               const ssd_layout* layout, const void* x, const void* d_raw, float d_init,
+               const void* B, const void* C, const float* init_state, const int32_t* cu_seqlens,
+               int32_t reverse, void* y, float* final_state, void* workspace,
+               size_t workspace_bytes, void* stream) {
     if (mask & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_SHAPE;
     Plan pl;
-    const int st = make_plan(dims, &pl);
+    const int st = make_plan(dims, tuning, &pl);
     if (st != SSD_OK) return st;
     const ssd_dims& d = *dims;
     const int64_t T = (int64_t)d.batch * d.seqlen;
@@ -369,14 +419,21 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     if (d.nseq > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
     if (d.nseq == 0 && cu_seqlens) return SSD_ERR_SHAPE;
     if (reverse != 0 && reverse != 1) return SSD_ERR_SHAPE;
+    const ssd_layout lay = resolve_layout(d, layout);
+    const int lc = check_layout(d, lay, false);
+    if (lc != SSD_OK) return lc;
     const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
-    const int64_t per_unit = 16 / esz;
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y)) return SSD_ERR_ALIGN;
     if ((uintptr_t)d_raw % esz) return SSD_ERR_ALIGN;  // read one element per lane
-    if (y_token_stride % per_unit != 0 || y_head_stride % per_unit != 0) return SSD_ERR_ALIGN;
-    if (y_token_stride < 0 || y_head_stride < 0) return SSD_ERR_SHAPE;
-    if (y_token_stride > ((int64_t)1 << 24)) return SSD_ERR_SHAPE;
     if (((uintptr_t)init_state & 3u) || ((uintptr_t)final_state & 3u)) return SSD_ERR_ALIGN;
+    const int64_t S = d.nseq > 0 ? d.nseq : d.batch;
+    const size_t state_bytes = (size_t)S * d.nheads * d.headdim * d.d_state * sizeof(float);
+    const int alias = state_alias(init_state, final_state, state_bytes);
+    if (alias < 0) return SSD_ERR_OVERLAP;
+    // final_state written over init_state: only the separate pass reads each
+    // initial state entry before the same thread writes its final value (the
+    // fold of plans 1 and 2 reads init_state in every span's workgroup)
+    if (alias > 0) pl.fuse = 0;
     if (pl.total > 0) {
         if (!workspace || workspace_bytes < pl.total) return SSD_ERR_WORKSPACE;
         if ((uintptr_t)workspace % kAlign) return SSD_ERR_ALIGN;
@@ -403,10 +460,16 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.states = ws + pl.off_states;
     p.decay = (float*)(ws + pl.off_decay);
     p.L = d.seqlen;
-    p.ys_t = y_token_stride;
-    p.ys_h = y_head_stride;
-    p.xs_t = (int64_t)d.nheads * d.headdim;
-    p.xs_h = d.headdim;
+    p.ys_t = lay.y_token;
+    p.ys_h = lay.y_head;
+    p.xs_t = lay.x_token;
+    p.xs_h = lay.x_head;
+    p.ds_t = lay.d_raw_token;
+    p.ds_h = lay.d_raw_head;
+    p.bs_t = lay.B_token;
+    p.bs_g = lay.B_group;
+    p.cs_t = lay.C_token;
+    p.cs_g = lay.C_group;
     p.nspan = pl.nspan;
     p.batch = d.batch;
     p.H = d.nheads;
@@ -422,6 +485,7 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
     p.reverse = reverse;
     p.fuse_pass = pl.fuse;
     p.hw_npb = pl.hw_npb;
+    p.state_f32 = pl.state_f32;
     p.sync = (uint32_t*)(ws + pl.off_sync);
     p.d_init = d_init;
 
@@ -447,6 +511,11 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     if (mask & SSD_STAGE_SCAN) {
+        if (pl.fuse == 2) {
+            // the fused launch's chain words and flags start from zero
+            e = ssd::launch_fused_reset(p.sync, pl.nsync, s);
+            if (e != hipSuccess) return SSD_ERR_HIP;
+        }
         e = pl.hw_npb ? ssd::launch_hw_scan(p, d.d_state, s)
                       : ssd::launch_span_scan(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
@@ -456,18 +525,29 @@ int ssd_fwd_stages(uint32_t mask, const ssd_dims* dims, const void* x, const voi
 
 size_t ssd_bwd_workspace_bytes(const ssd_dims* dims) {
     BPlan bp;
-    if (make_bwd_plan(dims, &bp) != SSD_OK) return 0;
+    if (make_bwd_plan(dims, nullptr, &bp) != SSD_OK) return 0;
     return bp.total;
 }
 
-int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init, const void* B,
-            const void* C, const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
-            const void* y, int64_t y_token_stride, int64_t y_head_stride, const void* dy,
-            int64_t dy_token_stride, int64_t dy_head_stride, const float* d_final, void* dx,
-            void* dd_raw, void* dB, void* dC, float* dinit_state, float* dd_init, void* workspace,
-            size_t workspace_bytes, void* stream) {
+int ssd_bwd(const ssd_dims* dims, const ssd_layout* layout, const void* x, const void* d_raw,
+            float d_init, const void* B, const void* C, const float* init_state,
+            const int32_t* cu_seqlens, int32_t reverse, const void* y, const void* dy,
+            const float* d_final, void* dx, void* dd_raw, void* dB, void* dC,
+            float* dinit_state, float* dd_init, void* workspace, size_t workspace_bytes,
+            void* stream) {
+    return ssd_bwd_ex(dims, nullptr, layout, x, d_raw, d_init, B, C, init_state, cu_seqlens,
+                      reverse, y, dy, d_final, dx, dd_raw, dB, dC, dinit_state, dd_init, workspace,
+                      workspace_bytes, stream);
+}
+
+int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout* layout,
+               const void* x, const void* d_raw, float d_init, const void* B, const void* C,
+               const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+               const void* y, const void* dy, const float* d_final, void* dx, void* dd_raw,
+               void* dB, void* dC, float* dinit_state, float* dd_init, void* workspace,
+               size_t workspace_bytes, void* stream) {
     BPlan bp;
-    const int st = make_bwd_plan(dims, &bp);
+    const int st = make_bwd_plan(dims, tuning, &bp);
     if (st != SSD_OK) return st;
     const ssd_dims& d = *dims;
     const int64_t T = (int64_t)d.batch * d.seqlen;
@@ -476,19 +556,22 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     if (d.nseq > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
     if (d.nseq == 0 && cu_seqlens) return SSD_ERR_SHAPE;
     if (reverse != 0 && reverse != 1) return SSD_ERR_SHAPE;
+    const ssd_layout lay = resolve_layout(d, layout);
+    const int lc = check_layout(d, lay, true);
+    if (lc != SSD_OK) return lc;
     const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
-    const int64_t per_unit = 16 / esz;
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(dy) ||
         !aligned16(dx) || !aligned16(dB) || !aligned16(dC))
         return SSD_ERR_ALIGN;
     if (((uintptr_t)d_raw % esz) || ((uintptr_t)dd_raw % esz)) return SSD_ERR_ALIGN;
-    for (int64_t v : {y_token_stride, y_head_stride, dy_token_stride, dy_head_stride}) {
-        if (v % per_unit != 0) return SSD_ERR_ALIGN;
-        if (v < 0 || v > ((int64_t)1 << 24)) return SSD_ERR_SHAPE;
-    }
     if (((uintptr_t)init_state & 3u) || ((uintptr_t)d_final & 3u) || ((uintptr_t)dinit_state & 3u) ||
         ((uintptr_t)dd_init & 3u))
         return SSD_ERR_ALIGN;
+    const int64_t S = d.nseq > 0 ? d.nseq : d.batch;
+    const size_t state_bytes = (size_t)S * d.nheads * d.headdim * d.d_state * sizeof(float);
+    // the output-gradient pass reads each d_final entry before the same
+    // thread writes its dinit_state entry, so the two may be one buffer
+    if (state_alias(d_final, dinit_state, state_bytes) < 0) return SSD_ERR_OVERLAP;
     if (!workspace || workspace_bytes < bp.total) return SSD_ERR_WORKSPACE;
     if ((uintptr_t)workspace % kAlign) return SSD_ERR_ALIGN;
     hipStream_t s = (hipStream_t)stream;
@@ -513,8 +596,14 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     pa.states = ws + bp.off_sa;
     pa.decay = (float*)(ws + bp.off_da);
     pa.L = d.seqlen;
-    pa.xs_t = (int64_t)d.nheads * d.headdim;
-    pa.xs_h = d.headdim;
+    pa.xs_t = lay.x_token;
+    pa.xs_h = lay.x_head;
+    pa.ds_t = lay.d_raw_token;
+    pa.ds_h = lay.d_raw_head;
+    pa.bs_t = lay.B_token;
+    pa.bs_g = lay.B_group;
+    pa.cs_t = lay.C_token;
+    pa.cs_g = lay.C_group;
     pa.nspan = bp.nchunk;
     pa.batch = d.batch;
     pa.H = d.nheads;
@@ -544,9 +633,11 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     // The two directions are independent: each kernel pair is one launch.
     ssd::KParams pg = pa;
     pg.x = dy;
-    pg.xs_t = dy_token_stride;
-    pg.xs_h = dy_head_stride;
+    pg.xs_t = lay.dy_token;
+    pg.xs_h = lay.dy_head;
     pg.B = C;
+    pg.bs_t = lay.C_token;
+    pg.bs_g = lay.C_group;
     pg.init = d_final;
     pg.final_state = dinit_state;
     pg.states = ws + bp.off_sb;
@@ -559,7 +650,7 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     // set-up.  With cu_seqlens the walks follow a second span table of
     // four-chunk spans, and the chunk slots are the per-chunk table's.
     ssd::KParams pa4 = pa, pg4 = pg;
-    if (getenv_int("SSD_BWD_STATE_CHUNKS", 4) == 4) {
+    if (bp.state_chunks == 4) {
         if (d.nseq > 0) {
             e = ssd::launch_span_table(cu_seqlens, d.nseq, T, 4, bp.nspan4,
                                        (int32_t*)(ws + bp.off_cu4), (int32_t*)(ws + bp.off_spoff4),
@@ -604,12 +695,18 @@ int ssd_bwd(const ssd_dims* dims, const void* x, const void* d_raw, float d_init
     q.table = pa.table;
     q.L = d.seqlen;
     q.ntok = T;
-    q.xs_t = (int64_t)d.nheads * d.headdim;
-    q.xs_h = d.headdim;
-    q.ys_t = y_token_stride;
-    q.ys_h = y_head_stride;
-    q.gs_t = dy_token_stride;
-    q.gs_h = dy_head_stride;
+    q.xs_t = lay.x_token;
+    q.xs_h = lay.x_head;
+    q.ys_t = lay.y_token;
+    q.ys_h = lay.y_head;
+    q.gs_t = lay.dy_token;
+    q.gs_h = lay.dy_head;
+    q.ds_t = lay.d_raw_token;
+    q.ds_h = lay.d_raw_head;
+    q.bs_t = lay.B_token;
+    q.bs_g = lay.B_group;
+    q.cs_t = lay.C_token;
+    q.cs_g = lay.C_group;
     q.nchunk = bp.nchunk;
     q.batch = d.batch;
     q.H = d.nheads;

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     const int hpg = p.H / p.G;
     const int h0 = grp * hpg + sub * p.hs;
     const int h1 = min(h0 + p.hs, (grp + 1) * hpg);
-    const int GN = p.G * N;
+    const int GN = p.G * N;  // token stride of the dB / dC partials
     // The loop runs over units (head, 64-column group of the headdim), head
     // by head.  Everything but dx is linear in the contributions of the
     // column groups -- the only sum over the headdim inside a chunk, dy X^T,
@@ -293,14 +293,17 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     const int P = p.P, npg = (P + kPGroup - 1) / kPGroup;
     const int nunit = (h1 - h0) * npg;
     auto ucols = [&](int u) { return min(kPGroup, P - kPGroup * (u % npg)); };
-    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.bs, (const T*)p.B + tb0 * GN + grp * N,
-                                                         dir * GN, wave, clen, N, lane);
-    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.cs, (const T*)p.C + tb0 * GN + grp * N,
-                                                         dir * GN, wave, clen, N, lane);
+    // token strides (the host keeps them <= 2^24)
+    const int BS = (int)p.bs_t, CS = (int)p.cs_t;
+    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.bs, (const T*)p.B + tb0 * BS + grp * p.bs_g,
+                                                         dir * BS, wave, clen, N, lane);
+    issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.cs, (const T*)p.C + tb0 * CS + grp * p.cs_g,
+                                                         dir * CS, wave, clen, N, lane);
     // d_raw of every head of the subset, one token per lane (a bf16 value in
     // the low half of its 32-bit slot)
     for (int i = wave; i < h1 - h0; i += kBWaves) {
-        const void* src = (const void*)((const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.H + h0 + i);
+        const void* src = (const void*)((const T*)p.d_raw + tok(lane < clen ? lane : 0) * p.ds_t +
+                                        (int64_t)(h0 + i) * p.ds_h);
         auto* lds = (__attribute__((address_space(3))) void*)sm.dr[i];
         if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
         else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         dd_acc = u % npg == 0 ? gr : dd_acc + gr;
         if (u % npg == npg - 1) {
             dd_val = dd_acc;
-            dd_at = in ? tok(s) * p.H + h : -1;
+            dd_at = in ? tok(s) * p.ds_t + (int64_t)h * p.ds_h : -1;
         }
         ddi += in ? gr : 0.f;
     };
@@ -645,10 +648,13 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* pb, const float* pc,
                                                          int nsub, int64_t n4, int64_t nblk,
-                                                         T* dB, T* dC, const float* ddi_part,
-                                                         int64_t nddi, float* dd_init) {
+                                                         T* dB, T* dC, int64_t bs_t, int64_t bs_g,
+                                                         int64_t cs_t, int64_t cs_g, int GN4, int N4,
+                                                         const float* ddi_part, int64_t nddi,
+                                                         float* dd_init) {
     const int64_t blk = blockIdx.x;
     if (blk < 2 * nblk) {
+        // four consecutive entries (token, group, 4 n4 .. +3) of dB or dC
         const bool second = blk >= nblk;
         const float* part = second ? pc : pb;
         T* out = second ? dC : dB;
@@ -656,7 +662,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* pb, const 
         if (i >= n4) return;
         f32x4 acc = *(const f32x4*)(part + 4 * i);
         for (int k = 1; k < nsub; ++k) acc += *(const f32x4*)(part + 4 * (k * n4 + i));
-        store4(out + 4 * i, acc);
+        const int64_t tk = i / GN4;
+        const int r = (int)(i - tk * GN4), gg = r / N4, n = 4 * (r - gg * N4);
+        store4(out + tk * (second ? cs_t : bs_t) + gg * (second ? cs_g : bs_g) + n, acc);
         return;
     }
     __shared__ float sh[256];
@@ -711,10 +719,12 @@ hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, fl
     const int64_t nddi = p.nchunk * p.G * p.nsub;
     if (dtype == 1)
         hipLaunchKernelGGL(bwd_reduce_kernel<bf16>, dim3((unsigned)grid), dim3(256), 0, s, p.dB_part,
-                           p.dC_part, p.nsub, n4, nblk, (bf16*)dB, (bf16*)dC, p.ddi_part, nddi, dd_init);
+                           p.dC_part, p.nsub, n4, nblk, (bf16*)dB, (bf16*)dC, p.bs_t, p.bs_g, p.cs_t,
+                           p.cs_g, p.G * p.N / 4, p.N / 4, p.ddi_part, nddi, dd_init);
     else
         hipLaunchKernelGGL(bwd_reduce_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, p.dB_part,
-                           p.dC_part, p.nsub, n4, nblk, (float*)dB, (float*)dC, p.ddi_part, nddi, dd_init);
+                           p.dC_part, p.nsub, n4, nblk, (float*)dB, (float*)dC, p.bs_t, p.bs_g, p.cs_t,
+                           p.cs_g, p.G * p.N / 4, p.N / 4, p.ddi_part, nddi, dd_init);
     return hipGetLastError();
 }
 

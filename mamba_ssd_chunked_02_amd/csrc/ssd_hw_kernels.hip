@@ -266,12 +266,13 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1)
     const int nvb = max(0, min(NPB, (pgw - 16 * blk0) / 16));  // blocks inside the headdim
 
     const int dir = p.reverse ? -1 : 1;
-    const int XS = (int)p.xs_t, GN = p.G * N;
+    // token strides (the host keeps them <= 2^24)
+    const int XS = (int)p.xs_t, BS = (int)p.bs_t, CS = (int)p.cs_t, DS = (int)p.ds_t;
     const int grp = (int)((int64_t)h0 * p.G / p.H);
     const bf16* const xg = (const bf16*)p.x + (int64_t)h * p.xs_h + pcol0;
-    const bf16* const bg = (const bf16*)p.B + (int64_t)grp * N;
-    const bf16* const cg = (const bf16*)p.C + (int64_t)grp * N;
-    const bf16* const dg = (const bf16*)p.d_raw + h;
+    const bf16* const bg = (const bf16*)p.B + (int64_t)grp * p.bs_g;
+    const bf16* const cg = (const bf16*)p.C + (int64_t)grp * p.cs_g;
+    const bf16* const dg = (const bf16*)p.d_raw + (int64_t)h * p.ds_h;
     const int64_t cj0 = (int64_t)chunk0 * kChunk;
     const int64_t tb0 = start + (p.reverse ? len - 1 - cj0 : cj0);
     const int dstep = dir * kChunk;
@@ -279,9 +280,9 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1)
     auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(c * dstep); };
     auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
     const bf16* const xc0 = xg + tb0 * XS;
-    const bf16* const bc0 = bg + tb0 * GN;
-    const bf16* const cc0 = cg + tb0 * GN;
-    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * GN;
+    const bf16* const bc0 = bg + tb0 * BS;
+    const bf16* const cc0 = cg + tb0 * CS;
+    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * BS, ccs = (int64_t)dstep * CS;
 
     // Chunk c's tiles: the waves of a head split its X tile, all waves split
     // B and C.  d_raw of a chunk: the head's first wave, one token per lane.
@@ -289,13 +290,13 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1)
                            bf16* __restrict__ cdst) {
         const int cl = clen_of(c);
         issue_tile<Cf::XIW, 1, Cf::XI>(xdst, xc0 + c * xcs, dir * XS, wc * Cf::XIW, cl, pgw, lane);
-        issue_tile<Cf::BIW, NW, Cf::BI>(bdst, bc0 + c * bcs, dir * GN, wave, cl, N, lane);
+        issue_tile<Cf::BIW, NW, Cf::BI>(bdst, bc0 + c * bcs, dir * BS, wave, cl, N, lane);
         if constexpr (SCAN)
-            issue_tile<Cf::BIW, NW, Cf::BI>(cdst, cc0 + c * bcs, dir * GN, wave, cl, N, lane);
+            issue_tile<Cf::BIW, NW, Cf::BI>(cdst, cc0 + c * ccs, dir * CS, wave, cl, N, lane);
     };
     auto issue_dr = [&](int c, uint32_t* __restrict__ ddst) {
         const int cl = clen_of(c);
-        const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * p.H);
+        const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * DS);
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)ddst, 2, 0, 0);
     };
 

@@ -33,6 +33,9 @@ struct KParams {
     int64_t ys_t, ys_h;     // y strides (elements)
     int64_t xs_t, xs_h;     // x strides (elements): token, head (H*P and P
                             // for a contiguous x)
+    int64_t ds_t, ds_h;     // d_raw strides: token, head (H and 1)
+    int64_t bs_t, bs_g;     // B strides: token, group (G*N and N)
+    int64_t cs_t, cs_g;     // C strides: token, group
     int64_t nspan;          // span slots (grid extent)
     int32_t batch, H, P, G, N;
     int32_t nseq;           // 0 = batch mode
@@ -63,6 +66,8 @@ struct KParams {
                             // (varlen)
     const int32_t* chunk_slot;  // (varlen, chunk_out) first chunk slot of each
                                 // sequence
+    int32_t state_f32;      // span states stored in float32 whatever the input
+                            // type (span kernels, plans 0 and 1)
     float d_init;
 };
 
@@ -77,8 +82,8 @@ struct BParams {
     const void* dy;         // dL/dy (strides gs_t, gs_h)
     const void* hprev;      // [nchunk][H][P*N] state entering each chunk
     const void* gout;       // [nchunk][H][P*N] dL/d(state leaving each chunk)
-    void* dx;               // [b, L, H, P]
-    void* dd_raw;           // [b, L, H]
+    void* dx;               // [b, L, H, P], strided like x
+    void* dd_raw;           // [b, L, H], strided like d_raw
     float* dB_part;         // [nsub][ntok][G][N] per head subset
     float* dC_part;
     float* ddi_part;        // [nchunk * G * nsub] per workgroup
@@ -86,6 +91,9 @@ struct BParams {
     const int4* table;      // [nchunk] {seq, chunk, 1, 0} (varlen)
     int64_t L, ntok;        // tokens per batch row, b * L
     int64_t xs_t, xs_h, ys_t, ys_h, gs_t, gs_h;
+    int64_t ds_t, ds_h;     // d_raw (and dd_raw) strides: token, head
+    int64_t bs_t, bs_g;     // B (and dB) strides: token, group
+    int64_t cs_t, cs_g;     // C (and dC) strides: token, group
     int64_t nchunk;         // chunk slots (grid extent / G / nsub)
     int32_t batch, H, P, G, N;
     int32_t nseq;
@@ -100,14 +108,18 @@ hipError_t launch_bwd_chunk(const BParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_reduce(const BParams& p, int dtype, void* dB, void* dC, float* dd_init,
                              hipStream_t s);
 
+// Zero the fused launch's chain words and flags (and the header's timeout
+// count) before it runs, so each fused call starts from a known state.
+hipError_t launch_fused_reset(uint32_t* sync, int64_t nwords, hipStream_t s);
+
 // Most spans per sequence for which span_scan forms the incoming states
 // itself (each workgroup folds all earlier spans of its sequence).
 constexpr int kFuseSpans = 16;
 
 // The workspace header: its first 256 bytes, of which word 2 counts the
 // fused launch's bounded flag waits that ran out.  The fused launch keeps
-// its ticket/epoch words and flags after it; all are zero before the first
-// call and left ready for the next call of the same sizes by every call.
+// its ticket/epoch words and flags after it; a reset kernel zeroes them
+// (and word 2) before every fused launch.
 constexpr int kSyncTimeouts = 2;
 constexpr int kSyncHeader = 64;
 // Polls (each followed by a 64-cycle sleep) one workgroup spends at most

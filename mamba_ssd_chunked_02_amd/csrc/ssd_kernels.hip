@@ -294,15 +294,16 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
     // Token of row r of chunk c: tok0(c) + dir * r.
     const int dir = p.reverse ? -1 : 1;
-    const int XS = (int)p.xs_t, GN = p.G * N;
+    // token strides (the host keeps them <= 2^24)
+    const int XS = (int)p.xs_t, BS = (int)p.bs_t, CS = (int)p.cs_t, DS = (int)p.ds_t;
     const int grp = (int)((int64_t)h0 * p.G / p.H);
     // Every wave computes, with a valid head even in a quad without one or
     // past the headdim; only active waves store what they computed.
     const int hc = live ? h : h0;
     const T* const xg = (const T*)p.x + (int64_t)hc * p.xs_h + pcol0;
-    const T* const bg = (const T*)p.B + (int64_t)grp * N;
-    const T* const cg = (const T*)p.C + (int64_t)grp * N;
-    const T* const dg = (const T*)p.d_raw + hc;
+    const T* const bg = (const T*)p.B + (int64_t)grp * p.bs_g;
+    const T* const cg = (const T*)p.C + (int64_t)grp * p.cs_g;
+    const T* const dg = (const T*)p.d_raw + (int64_t)hc * p.ds_h;
     // Row 0 of chunk c is token tb0 + c * dstep; its tokens left in the
     // sequence are rem0 - 64c.
     const int64_t cj0 = (int64_t)chunk0 * kChunk;
@@ -313,27 +314,27 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
     // chunk c's row-0 pointers: base at chunk 0 plus c chunk steps
     const T* const xc0 = xg + tb0 * XS;
-    const T* const bc0 = bg + tb0 * GN;
-    const T* const cc0 = cg + tb0 * GN;
-    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * GN;
+    const T* const bc0 = bg + tb0 * BS;
+    const T* const cc0 = cg + tb0 * CS;
+    const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * BS, ccs = (int64_t)dstep * CS;
     // Chunk c's X tile (wave w4 loads its own 16-column block) and this
     // wave's share of the B tile.
     auto issue_xb = [&](int c, T* __restrict__ xdst, T* __restrict__ bdst) {
         const int cl = clen_of(c);
         issue_tile<W, 1, XI>(xdst, xc0 + c * xcs, dir * XS, w4 * W, cl, pgw, lane);
-        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + c * bcs, dir * GN, wave, cl, N,
+        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + c * bcs, dir * BS, wave, cl, N,
                                                         lane);
     };
     // This wave's share of chunk c's C tile (scan).
     auto issue_c = [&](int c, T* __restrict__ cdst) {
         if constexpr (SCANL)
-            issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cc0 + c * bcs, dir * GN, wave,
+            issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(cdst, cc0 + c * ccs, dir * CS, wave,
                                                             clen_of(c), N, lane);
     };
     // The quad head's d_raw of chunk c, one token per lane.
     auto issue_d = [&](int c, uint32_t* __restrict__ ddst) {
         const int cl = clen_of(c);
-        const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * p.H);
+        const void* src = (const void*)(dg + (tok0(c) + dir * (lane < cl ? lane : 0)) * DS);
         auto* lds = (__attribute__((address_space(3))) void*)ddst;
         if constexpr (sizeof(T) == 2) __builtin_amdgcn_global_load_lds(src, lds, 2, 0, 0);
         else __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
@@ -356,6 +357,10 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
     auto state_ptr = [&](int64_t sp) -> T* {
         return (T*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
+    };
+    // the same slot when span states are stored in float32 (plans 0 and 1)
+    auto state_ptr_f = [&](int64_t sp) -> float* {
+        return (float*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
     };
     // (chunk_out) state slot of the span's first chunk: ceil(L / 64) slots
     // per sequence in batch mode, from the per-chunk table's offsets with
@@ -623,8 +628,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
             return;
         }
         if (active) {
+            if (p.state_f32) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) store4(state_ptr(span) + state_off(pb, nb, lane, NB), Hs[nb]);
+                for (int nb = 0; nb < NB; ++nb) store4(state_ptr_f(span) + state_off(pb, nb, lane, NB), Hs[nb]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) store4(state_ptr(span) + state_off(pb, nb, lane, NB), Hs[nb]);
+            }
         }
         if (pg == 0 && w4 == 0 && live && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
         return;
@@ -673,8 +683,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         // place of the span state, or folded here span by span
         if (active) {
             if (!folds) {
+                if (p.state_f32) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(state_ptr(span) + state_off(pb, nb, lane, NB));
+                    for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(state_ptr_f(span) + state_off(pb, nb, lane, NB));
+                } else {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) Hs[nb] = load4(state_ptr(span) + state_off(pb, nb, lane, NB));
+                }
             } else {
                 if (p.init) {
 #pragma unroll
@@ -684,9 +699,15 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                 }
                 for (int64_t sj = span - kin; sj < span; ++sj) {
                     const float a = p.decay[sj * p.H + h];
+                    if (p.state_f32) {
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        Hs[nb] = a * Hs[nb] + load4(state_ptr(sj) + state_off(pb, nb, lane, NB));
+                        for (int nb = 0; nb < NB; ++nb)
+                            Hs[nb] = a * Hs[nb] + load4(state_ptr_f(sj) + state_off(pb, nb, lane, NB));
+                    } else {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            Hs[nb] = a * Hs[nb] + load4(state_ptr(sj) + state_off(pb, nb, lane, NB));
+                    }
                 }
             }
         }
@@ -840,6 +861,14 @@ __global__ __launch_bounds__(256) void state_pass_pair_kernel(KParams pa, KParam
     else state_pass_body<TS>(pb, ((int64_t)blockIdx.x - na) * 256 + threadIdx.x);
 }
 
+// Zero words [0, nwords) of the workspace header and the fused launch's
+// chain words and flags (a fill kernel rather than a memset, so the call
+// can be captured in a graph).
+__global__ __launch_bounds__(256) void fused_reset_kernel(uint32_t* sync, int64_t nwords) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < nwords) sync[i] = 0u;
+}
+
 // One workgroup: sanitize cu_seqlens (clamped running maximum, first entry
 // 0), count each sequence's spans, prefix-sum them and write the span table.
 // Tail slots up to nspan are marked empty (seq = -1).
@@ -985,6 +1014,13 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T, int
     return hipGetLastError();
 }
 
+hipError_t launch_fused_reset(uint32_t* sync, int64_t nwords, hipStream_t s) {
+    if (nwords <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fused_reset_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s,
+                       sync, nwords);
+    return hipGetLastError();
+}
+
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s) {
     return p.wmode ? launch_span<kModeStateGrad>(p, dtype, N, s) : launch_span<kModeState>(p, dtype, N, s);
 }
@@ -1037,11 +1073,12 @@ hipError_t launch_state_pass_pair(const KParams& pa, const KParams& pb, int dtyp
 
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s) {
     const int64_t S = p.nseq ? p.nseq : p.batch;
-    const int V = dtype == 1 ? 8 : 4;
+    const bool s16 = dtype == 1 && !p.state_f32;  // span states stored in bf16
+    const int V = s16 ? 8 : 4;
     const int64_t n = S * p.H * (int64_t)p.P * p.N / V;
     if (n == 0) return hipSuccess;
     const dim3 grid((unsigned)((n + 255) / 256));
-    if (dtype == 1)
+    if (s16)
         hipLaunchKernelGGL(state_pass_kernel<bf16>, grid, dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL(state_pass_kernel<float>, grid, dim3(256), 0, s, p);

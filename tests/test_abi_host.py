@@ -49,7 +49,7 @@ def test_abi_version(m):
 
 def test_status_strings(m):
     codes = [int(v) for v in re.findall(r"SSD_(?:OK|ERR_\w+)\s*=\s*(-?\d+)", open(HEADER).read())]
-    assert 0 in codes and -7 in codes
+    assert 0 in codes and -7 in codes and -9 in codes
     for c in codes:
         s = m.ssd_status_string(c)
         assert s and "unknown ssd status" not in s
@@ -74,16 +74,30 @@ def test_workspace_bytes(m):
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below is rejected
 
 
-def call(m, dims, **kw):
+def lay(m, dims, **kw):
+    """A layout for dims (contiguous unless fields are given)."""
+    H, P, G, N = dims.nheads, dims.headdim, dims.ngroups, dims.d_state
+    l = m.SsdLayout(H * P, P, H, 1, G * N, N, G * N, N, H * P, P, H * P, P)
+    for k, v in kw.items():
+        setattr(l, k, v)
+    return l
+
+
+def call(m, dims, layout=None, tuning=None, **kw):
     args = dict(x=FAKE, d_raw=FAKE, d_init=-4.6, B=FAKE, C=FAKE, init=None, cu=None, reverse=0,
-                y=FAKE, yst=(dims.nheads * dims.headdim) if dims else 64,
-                ysh=dims.headdim if dims else 16, fin=None, ws=FAKE, wsb=1 << 40, stream=None)
+                y=FAKE, fin=None, ws=FAKE, wsb=1 << 40, stream=None)
     args.update(kw)
     vp = lambda v: None if v is None else ctypes.c_void_p(v)
-    return m.library().ssd_fwd(
-        ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)(), vp(args["x"]), vp(args["d_raw"]), args["d_init"], vp(args["B"]),
-        vp(args["C"]), vp(args["init"]), vp(args["cu"]), args["reverse"], vp(args["y"]),
-        args["yst"], args["ysh"], vp(args["fin"]), vp(args["ws"]), args["wsb"], vp(args["stream"]))
+    a = args
+    rest = (vp(a["x"]), vp(a["d_raw"]), a["d_init"], vp(a["B"]), vp(a["C"]), vp(a["init"]),
+            vp(a["cu"]), a["reverse"], vp(a["y"]), vp(a["fin"]), vp(a["ws"]), a["wsb"],
+            vp(a["stream"]))
+    dp = ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)()
+    lp = ctypes.byref(layout) if layout is not None else ctypes.POINTER(m.SsdLayout)()
+    if tuning is None:
+        return m.library().ssd_fwd(dp, lp, *rest)
+    t = m.make_tuning(tuning)
+    return m.library().ssd_fwd_ex(15, dp, ctypes.byref(t), lp, *rest)
 
 
 needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
@@ -109,10 +123,57 @@ def test_rejects_bad_arguments(m):
     assert call(m, ok, x=FAKE + 8) == -4                               # ALIGN
     assert call(m, ok, y=FAKE + 2) == -4
     assert call(m, ok, d_raw=FAKE + 1) == -4                           # d_raw: bf16 elements
-    assert call(m, ok, yst=64 * 2 + 4) == -4
     assert call(m, ok, ws=None) == -6                                  # WORKSPACE
     assert call(m, ok, wsb=16) == -6
     assert call(m, ok, ws=FAKE + 16) == -4
+
+
+@needs_no_gpu
+def test_rejects_bad_strides(m):
+    """Rows of x, B, C and y are 16-byte units; every stride is >= 0 and
+    <= 2^24 elements; d_raw's strides may be any element count."""
+    ok = m.make_dims(1, 128, 2, 64, 128)
+    for field in ("x_token", "x_head", "B_token", "B_group", "C_token", "C_group",
+                  "y_token", "y_head"):
+        assert call(m, ok, layout=lay(m, ok, **{field: 4 + 128})) == -4, field   # 8 bytes off
+        assert call(m, ok, layout=lay(m, ok, **{field: -8})) == -2, field
+        assert call(m, ok, layout=lay(m, ok, **{field: (1 << 24) + 8})) == -2, field
+    for field in ("d_raw_token", "d_raw_head"):
+        assert call(m, ok, layout=lay(m, ok, **{field: -1})) == -2, field
+        assert call(m, ok, layout=lay(m, ok, **{field: (1 << 24) + 1})) == -2, field
+    # an odd d_raw stride is fine: the call goes on to the workspace check
+    assert call(m, ok, layout=lay(m, ok, d_raw_token=1817, d_raw_head=3), ws=None) == -6
+
+
+@needs_no_gpu
+def test_rejects_partly_overlapping_states(m):
+    """final_state may be init_state itself (the separate pass reads each
+    entry before writing it), but not overlap it at another offset."""
+    ok = m.make_dims(1, 128, 2, 64, 128)
+    assert call(m, ok, init=FAKE, fin=FAKE + 4096) == -9
+    assert call(m, ok, init=FAKE + 4096, fin=FAKE) == -9
+    # the same buffer passes the overlap check (rejected later for the workspace)
+    assert call(m, ok, init=FAKE, fin=FAKE, ws=None) == -6
+    # disjoint buffers too
+    assert call(m, ok, init=FAKE, fin=FAKE + 2 * 128 * 64 * 4, ws=None) == -6
+
+
+@needs_no_gpu
+def test_rejects_bad_tuning(m):
+    ok = m.make_dims(1, 128, 2, 64, 128)
+    t = m.SsdTuning()
+    t.reserved[3] = 1
+    assert call(m, ok, tuning=t) == -2
+    assert call(m, ok, tuning={"kernel": 3}) == -2
+    assert call(m, ok, tuning={"chunks_per_span": 65}) == -2
+    assert call(m, ok, tuning={"state_pass": 4}) == -2
+    assert call(m, ok, tuning={"cols_per_wave": 48}) == -2
+    assert call(m, ok, tuning={"kernel": "hw", "cols_per_wave": 64}) == -2   # 64 needs d_state 64
+    assert call(m, ok, tuning={"heads_scan": 3}) == -2
+    assert call(m, m.make_dims(1, 128, 2, 64, 128, dtype=0), tuning={"kernel": "hw"}) == -5
+    assert call(m, ok, tuning={"state_f32": 1, "state_pass": "fused"}) == -2
+    varlen = m.make_dims(1, 128, 2, 64, 128, nseq=2)
+    assert call(m, varlen, tuning={"state_pass": "fold"}, cu=FAKE) == -2
 
 
 def test_binding_rejects_cpu_mismatch(m):
@@ -122,54 +183,106 @@ def test_binding_rejects_cpu_mismatch(m):
                   torch.zeros(1, 64, 1, 16))
 
 
-def test_plan_folds_state_pass_for_short_sequences(m, monkeypatch):
+def test_layout_of_projection_views(m):
+    """x, B, C and d_raw as views of one [b, L, H*P + 2*G*N + H] projection
+    buffer: the binding reads their strides into the layout."""
+    b, L, H, P, G, N = 2, 16, 3, 32, 1, 64
+    W = H * P + 2 * G * N + H
+    proj = torch.zeros(b, L, W, dtype=torch.bfloat16)
+    x = proj[..., :H * P].view(b, L, H, P)
+    B = proj[..., H * P:H * P + G * N].view(b, L, G, N)
+    C = proj[..., H * P + G * N:H * P + 2 * G * N].view(b, L, G, N)
+    dr = proj[..., H * P + 2 * G * N:]
+    l = m.layout_of(x, dr, B, C)
+    assert (l.x_token, l.x_head, l.B_token, l.B_group, l.C_token, l.C_group,
+            l.d_raw_token, l.d_raw_head) == (W, P, W, N, W, N, W, 1)
+    # every other token keeps batch rows L' token strides apart: allowed
+    m.layout_of(x[:, ::2], dr[:, ::2], B[:, ::2], C[:, ::2])
+    with pytest.raises(ValueError):          # batch rows not L tokens apart
+        m.layout_of(x[:, :L - 2], dr[:, :L - 2], B[:, :L - 2], C[:, :L - 2])
+
+
+def test_plan_folds_state_pass_for_short_sequences(m):
     """Batch mode with 1..8 spans per sequence folds the state pass into
     span_scan; packed sequences, longer ones and empty ones keep the three
-    launches; SSD_FUSE_PASS forces any of the three plans in batch mode."""
-    monkeypatch.delenv("SSD_FUSE_PASS", raising=False)
-    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
-    monkeypatch.setenv("SSD_KERNEL", "span")
+    launches; tuning.state_pass forces any of the three plans in batch mode."""
+    span = {"kernel": "span"}
     layer_dims = m.make_dims(2, 2048, 24, 64, 128)
-    layer = m.ssd_fwd_plan(layer_dims)
+    layer = m.ssd_fwd_plan(layer_dims, span)
     assert layer.chunks_per_span == 4 and layer.fused_pass == 1
-    long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 9, 2, 64, 128))
+    long = m.ssd_fwd_plan(m.make_dims(1, 64 * 4 * 9, 2, 64, 128), span)
     assert long.chunks_per_span == 4 and long.fused_pass == 0
-    varlen = m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3))
+    varlen = m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3), span)
     assert varlen.fused_pass == 0
-    assert m.ssd_fwd_plan(m.make_dims(2, 0, 2, 64, 128)).fused_pass == 0
+    assert m.ssd_fwd_plan(m.make_dims(2, 0, 2, 64, 128), span).fused_pass == 0
     for forced in (0, 1, 2):
-        monkeypatch.setenv("SSD_FUSE_PASS", str(forced))
-        assert m.ssd_fwd_plan(layer_dims).fused_pass == forced
-        assert m.ssd_fwd_plan(m.make_dims(1, 4096, 2, 64, 128, nseq=3)).fused_pass == 0
+        assert m.ssd_fwd_plan(layer_dims, {"kernel": "span", "state_pass": forced + 1}).fused_pass == forced
 
 
-def test_workspace_header_in_every_plan(m, monkeypatch):
+def test_workspace_header_in_every_plan(m):
     """Every plan reserves the 256-byte header at the start of the
     workspace; the fused plan adds one 8-byte ticket/epoch word per chain
     (sequence, head group, column group) and one 4-byte flag per
     workgroup."""
-    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    sizes = {}
-    for forced in (0, 1, 2):
-        monkeypatch.setenv("SSD_FUSE_PASS", str(forced))
-        sizes[forced] = m.ssd_fwd_workspace_bytes(m.make_dims(2, 2048, 24, 64, 128))
-    assert sizes[0] == sizes[1]
+    d = m.make_dims(2, 2048, 24, 64, 128)
+    sizes = {f: m.ssd_fwd_plan(d, {"kernel": "span", "state_pass": f + 1}).workspace_bytes
+             for f in (0, 1, 2)}
+    assert sizes[0] == sizes[1] == m.ssd_fwd_workspace_bytes(d)
     chains = 2 * 24  # sequences x heads x one column group
     nwg = chains * (2048 // 64 // 4)  # x spans per sequence
     assert sizes[2] - sizes[0] == -(-(chains * 8 + nwg * 4) // 256) * 256
     assert m.ssd_fwd_workspace_bytes(m.make_dims(2, 0, 2, 64, 128)) >= 256
 
-def test_plan_head_wave_kernels(m, monkeypatch):
+
+def test_state_f32_doubles_span_states(m):
+    """tuning.state_f32 stores the span states in float32: the state part of
+    the workspace doubles for bf16 inputs; fp32 inputs are unchanged."""
+    d = m.make_dims(2, 2048, 24, 64, 128)
+    a = m.ssd_fwd_plan(d, {"kernel": "span"})
+    b = m.ssd_fwd_plan(d, {"kernel": "span", "state_f32": 1})
+    assert (a.state_bytes, b.state_bytes) == (2, 4)
+    states = a.nspan * 24 * 64 * 128 * 2
+    assert b.workspace_bytes - a.workspace_bytes == states
+    f = m.make_dims(2, 2048, 24, 64, 128, dtype=0)
+    assert m.ssd_fwd_plan(f, {"state_f32": 1}).workspace_bytes == m.ssd_fwd_workspace_bytes(f)
+
+
+def test_plan_ignores_the_environment(m, monkeypatch):
+    """The library reads no tuning from the environment: setting the names
+    of the knobs it once had changes neither the plan nor the workspace."""
+    dims = [m.make_dims(2, 2048, 24, 64, 128), m.make_dims(1, 65536, 24, 64, 128, nseq=16),
+            m.make_dims(1, 1 << 20, 8, 192, 64)]
+    before = [(m.ssd_fwd_workspace_bytes(d), m.ssd_bwd_workspace_bytes(d),
+               tuple(getattr(m.ssd_fwd_plan(d), f) for f, _ in m.SsdPlanInfo._fields_[:10]))
+              for d in dims]
+    for k, v in {"SSD_KERNEL": "hw", "SSD_FUSE_PASS": "2", "SSD_SPAN_CHUNKS": "1",
+                 "SSD_HW_NPB": "4", "SSD_HW_HEADS": "1", "SSD_HW_HEADS_STATE": "1",
+                 "SSD_HEADS_STATE": "2", "SSD_HEADS_SCAN": "2", "SSD_BWD_HEADS": "1",
+                 "SSD_BWD_STATE_CHUNKS": "1"}.items():
+        monkeypatch.setenv(k, v)
+    after = [(m.ssd_fwd_workspace_bytes(d), m.ssd_bwd_workspace_bytes(d),
+              tuple(getattr(m.ssd_fwd_plan(d), f) for f, _ in m.SsdPlanInfo._fields_[:10]))
+             for d in dims]
+    assert before == after
+
+
+def test_library_reads_only_ssd_check():
+    """The only environment variable the library's sources read is SSD_CHECK."""
+    src = os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc")
+    names = set()
+    for f in os.listdir(src):
+        names |= set(re.findall(r'getenv\("(\w+)"\)', open(os.path.join(src, f)).read()))
+    assert names == {"SSD_CHECK"}
+
+
+def test_plan_head_wave_kernels(m):
     """Large bf16 problems with d_state 64 / 128 run the head-wave kernels
     with three launches and long spans; small ones, fp32, other d_state
-    values and SSD_KERNEL=span keep the span kernels; SSD_KERNEL=hw forces
-    the head-wave kernels."""
-    for v in ("SSD_FUSE_PASS", "SSD_SPAN_CHUNKS", "SSD_KERNEL", "SSD_HW_NPB", "SSD_HW_HEADS"):
-        monkeypatch.delenv(v, raising=False)
+    values and tuning.kernel = span keep the span kernels; tuning.kernel =
+    hw forces the head-wave kernels."""
     varlen = m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16))
     assert (varlen.head_wave, varlen.chunks_per_span, varlen.cols_per_wave, varlen.heads_per_wg,
-            varlen.fused_pass) == (1, 16, 32, 4, 0)
+            varlen.heads_per_state_wg, varlen.fused_pass) == (1, 16, 32, 4, 2, 0)
     bidir = m.ssd_fwd_plan(m.make_dims(1, 1 << 20, 8, 192, 64))
     assert (bidir.head_wave, bidir.chunks_per_span, bidir.cols_per_wave, bidir.heads_per_wg) == (1, 32, 32, 2)
     wide = m.ssd_fwd_plan(m.make_dims(1, 8192, 80, 64, 128))   # 10240 items: span kernels
@@ -177,28 +290,30 @@ def test_plan_head_wave_kernels(m, monkeypatch):
     assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).head_wave == 0   # layer: span kernels
     assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, dtype=0)).head_wave == 0
     assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 32)).head_wave == 0
-    monkeypatch.setenv("SSD_KERNEL", "hw")
-    small = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128))
+    small = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128), {"kernel": "hw"})
     assert small.head_wave == 1 and small.fused_pass == 0
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16)).head_wave == 0
+    assert m.ssd_fwd_plan(m.make_dims(1, 65536, 24, 64, 128, nseq=16),
+                          {"kernel": "span"}).head_wave == 0
+    shaped = m.ssd_fwd_plan(m.make_dims(1, 4096, 8, 64, 64),
+                            {"kernel": "hw", "cols_per_wave": 64, "heads_scan": 1,
+                             "chunks_per_span": 3})
+    assert (shaped.cols_per_wave, shaped.heads_per_wg, shaped.chunks_per_span) == (64, 1, 3)
 
 
-def call_bwd(m, dims, **kw):
-    H, P = (dims.nheads, dims.headdim) if dims else (2, 16)
+def call_bwd(m, dims, layout=None, **kw):
     args = dict(x=FAKE, d_raw=FAKE, d_init=-4.6, B=FAKE, C=FAKE, init=None, cu=None, reverse=0,
-                y=FAKE, yst=H * P, ysh=P, dy=FAKE, gst=H * P, gsh=P, dfin=None, dx=FAKE,
-                ddr=FAKE, dB=FAKE, dC=FAKE, dinit=None, ddi=None, ws=FAKE, wsb=1 << 40,
-                stream=None)
+                y=FAKE, dy=FAKE, dfin=None, dx=FAKE, ddr=FAKE, dB=FAKE, dC=FAKE, dinit=None,
+                ddi=None, ws=FAKE, wsb=1 << 40, stream=None)
     args.update(kw)
     vp = lambda v: None if v is None else ctypes.c_void_p(v)
     a = args
+    lp = ctypes.byref(layout) if layout is not None else ctypes.POINTER(m.SsdLayout)()
     return m.library().ssd_bwd(
-        ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)(), vp(a["x"]), vp(a["d_raw"]),
-        a["d_init"], vp(a["B"]), vp(a["C"]), vp(a["init"]), vp(a["cu"]), a["reverse"], vp(a["y"]),
-        a["yst"], a["ysh"], vp(a["dy"]), a["gst"], a["gsh"], vp(a["dfin"]), vp(a["dx"]),
-        vp(a["ddr"]), vp(a["dB"]), vp(a["dC"]), vp(a["dinit"]), vp(a["ddi"]), vp(a["ws"]),
-        a["wsb"], vp(a["stream"]))
+        ctypes.byref(dims) if dims else ctypes.POINTER(m.SsdDims)(), lp, vp(a["x"]),
+        vp(a["d_raw"]), a["d_init"], vp(a["B"]), vp(a["C"]), vp(a["init"]), vp(a["cu"]),
+        a["reverse"], vp(a["y"]), vp(a["dy"]), vp(a["dfin"]), vp(a["dx"]), vp(a["ddr"]),
+        vp(a["dB"]), vp(a["dC"]), vp(a["dinit"]), vp(a["ddi"]), vp(a["ws"]), a["wsb"],
+        vp(a["stream"]))
 
 
 def test_bwd_workspace_bytes(m):
@@ -209,6 +324,7 @@ def test_bwd_workspace_bytes(m):
     states = 2 * 64 * 24 * 64 * 128 * 2
     assert states < ws < states + 2 * 24 * 4096 * 128 * 4 + (1 << 20)
     assert ws % 256 == 0
+    assert m.ssd_fwd_plan(d).bwd_workspace_bytes == ws
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 192, 64)) > 0      # 3 column groups
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 64, 256)) == 0      # d_state 256
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 64, dtype=0)) == 0
@@ -216,14 +332,24 @@ def test_bwd_workspace_bytes(m):
     assert m.ssd_bwd_workspace_bytes(m.make_dims(1, 0, 2, 16, 16)) > 0         # empty input
 
 
-def test_bwd_head_subsets(m, monkeypatch):
+def test_bwd_plan_of_layer_workload(m):
+    """The layer workload (2 x 2048 tokens, 24 heads): 6 heads per gradient
+    workgroup, 4 head subsets of dB / dC partials, four-chunk chunk-state
+    walks."""
+    info = m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128))
+    assert (info.bwd_heads_per_wg, info.bwd_head_subsets, info.bwd_state_chunks) == (6, 4, 4)
+
+
+def test_bwd_head_subsets(m):
     """The gradient kernel's head subsets: the largest divisor of the group's
     heads that keeps >= 256 workgroups (one per CU) -- fewer subsets, smaller partials."""
-    few = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))   # 1024 chunks
-    monkeypatch.setenv("SSD_BWD_HEADS", "1")
-    many = m.ssd_bwd_workspace_bytes(m.make_dims(1, 64 * 1024, 24, 64, 128))
+    d = m.make_dims(1, 64 * 1024, 24, 64, 128)   # 1024 chunks
+    few = m.ssd_bwd_workspace_bytes(d)
+    many = m.ssd_fwd_plan(d, {"bwd_heads": 1}).bwd_workspace_bytes
     part = (24 - 1) * 2 * 64 * 1024 * 128 * 4   # 23 more subsets of dB and dC partials
     assert part <= many - few < part + (1 << 20)
+    with pytest.raises(m.SsdError):
+        m.ssd_fwd_plan(d, {"bwd_heads": 5})      # does not divide 24
 
 
 @needs_no_gpu
@@ -240,8 +366,10 @@ def test_bwd_rejects_bad_arguments(m):
     assert call_bwd(m, ok, reverse=3) == -2
     assert call_bwd(m, ok, dy=FAKE + 8) == -4                              # ALIGN
     assert call_bwd(m, ok, dx=FAKE + 4) == -4
-    assert call_bwd(m, ok, gst=64 * 2 + 4) == -4
-    assert call_bwd(m, ok, gst=1 << 25) == -2
+    assert call_bwd(m, ok, layout=lay(m, ok, dy_token=64 * 2 + 4)) == -4
+    assert call_bwd(m, ok, layout=lay(m, ok, dy_token=1 << 25)) == -2
     assert call_bwd(m, ok, ddr=FAKE + 1) == -4
+    assert call_bwd(m, ok, dfin=FAKE, dinit=FAKE + 256) == -9             # partial overlap
+    assert call_bwd(m, ok, dfin=FAKE, dinit=FAKE, ws=None) == -6          # same buffer: allowed
     assert call_bwd(m, ok, ws=None) == -6                                  # WORKSPACE
     assert call_bwd(m, ok, wsb=16) == -6

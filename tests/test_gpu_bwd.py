@@ -12,9 +12,10 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import cref
 from oracle import ssd_oracle as F
 from oracle import ssd_oracle_bwd as O
-from ssd_inputs import random_problem
+from ssd_inputs import WORKLOADS, make_inputs, make_inputs_device, random_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +37,7 @@ def _dev(t):
     return None if t is None else t.to(DEV)
 
 
-def bwd_case(ssd, p, reverse=False, with_final=True, seed=0, label=""):
+def bwd_case(ssd, p, reverse=False, with_final=True, seed=0, label="", tuning=None):
     dt = p["x"].dtype
     tol = BWD_TOL[dt]
     d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
@@ -50,14 +51,13 @@ def bwd_case(ssd, p, reverse=False, with_final=True, seed=0, label=""):
     dfin = torch.randn((S, H, N, P), generator=g) if with_final else None
     got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, _dev(dy),
                       init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], reverse=reverse,
-                      d_final=_dev(dfin))
+                      d_final=_dev(dfin), tuning=tuning)
     torch.cuda.synchronize()
     ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
                         init_state=p["init_state"], d_final=dfin, cu_seqlens=p["cu_seqlens"],
                         reverse=reverse)
     errs = {k: F.rel_err(got[k].float().cpu(), ref[k]) for k in KEYS}
-    errs["dd_init"] = abs(float(got["dd_init"].cpu()) - ref["dd_init"]) / max(
-        float(np.abs(ref["dd_raw"]).sum()), 1e-30)
+    errs["dd_init"] = dd_init_err(float(got["dd_init"].cpu()), ref)
     print(f"{label} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()) + f" tol={tol}",
           flush=True)
     for k in KEYS:
@@ -65,6 +65,15 @@ def bwd_case(ssd, p, reverse=False, with_final=True, seed=0, label=""):
     for k, v in errs.items():
         assert v <= tol, (k, v)
     return got, ref
+
+
+def dd_init_err(got, ref):
+    """Error of the d_init gradient, a sum of every d d_raw entry.  Each
+    summand carries the kernel's relative error, so the error of the sum is
+    bounded by that error times the sum of the summands' magnitudes, not
+    times the sum itself (the summands have both signs and largely cancel):
+    the error is taken relative to sum |d d_raw|, the sum's condition scale."""
+    return abs(got - ref["dd_init"]) / max(float(np.abs(ref["dd_raw"]).sum()), 1e-30)
 
 
 SHAPES = [
@@ -111,13 +120,12 @@ def test_bwd_no_state_gradients(ssd):
     bwd_case(ssd, p, with_final=False, label="bwd no-state")
 
 
-def test_bwd_head_subsets(ssd, monkeypatch):
-    """One head per workgroup (24 partials of dB / dC added) and all heads in
-    one workgroup give the same gradients within the bound."""
+def test_bwd_head_subsets(ssd):
+    """One head per workgroup (six partials of dB / dC added) and all heads
+    in one workgroup give the same gradients within the bound."""
     p = random_problem(317, 1, 256, 6, 64, 128, dtype="bf16", init_scale=0.5, d_init=-2.0)
-    for hs in ("1", "6"):
-        monkeypatch.setenv("SSD_BWD_HEADS", hs)
-        bwd_case(ssd, p, label=f"bwd heads/wg={hs}")
+    for hs in (1, 6):
+        bwd_case(ssd, p, label=f"bwd heads/wg={hs}", tuning={"bwd_heads": hs})
 
 
 def test_bwd_layer_shape(ssd):
@@ -189,7 +197,7 @@ def test_bwd_long_walks_weak_decay(ssd):
 
 
 @pytest.mark.parametrize("varlen", [False, True])
-def test_bwd_chunk_state_walks_bit_exact(ssd, monkeypatch, varlen):
+def test_bwd_chunk_state_walks_bit_exact(ssd, varlen):
     """Chunk-state workgroups that walk four chunks (restarting from a zero
     state at each) do per chunk exactly the arithmetic of one workgroup per
     chunk: every gradient is bit-identical between the two."""
@@ -205,11 +213,164 @@ def test_bwd_chunk_state_walks_bit_exact(ssd, monkeypatch, varlen):
     g = torch.Generator().manual_seed(3)
     dy = torch.randn(p["x"].shape, generator=g).to(torch.bfloat16).to(DEV)
     out = []
-    for chunks in ("4", "1"):
-        monkeypatch.setenv("SSD_BWD_STATE_CHUNKS", chunks)
+    for chunks in (4, 1):
         got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, dy,
-                          init_state=d["init_state"], cu_seqlens=d["cu_seqlens"])
+                          init_state=d["init_state"], cu_seqlens=d["cu_seqlens"],
+                          tuning={"bwd_state_chunks": chunks})
         torch.cuda.synchronize()
         out.append(got)
     for k in KEYS + ("dd_init",):
         assert torch.equal(out[0][k], out[1][k]), k
+
+
+def test_bwd_layer_workload_full(ssd):
+    """The layer workload at the size the benchmark times it (2 x 2048
+    tokens, 24 heads x headdim 64, d_state 128), every gradient on full
+    tensors against the C adjoint oracle, in the plan the benchmark runs:
+    six heads per gradient workgroup, four head subsets of dB / dC partials,
+    four-chunk chunk-state walks."""
+    w = WORKLOADS[2]
+    p = make_inputs(w)
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    info = ssd.ssd_fwd_plan(ssd.dims_for(d["x"], d["B"]))
+    assert (info.bwd_heads_per_wg, info.bwd_head_subsets, info.bwd_state_chunks) == (6, 4, 4)
+    y, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"])
+    g = torch.Generator().manual_seed(23)
+    dy = torch.randn(p["x"].shape, generator=g).to(torch.bfloat16)
+    dfin = torch.randn((2, 24, 128, 64), generator=g)
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, _dev(dy),
+                      d_final=_dev(dfin))
+    torch.cuda.synchronize()
+    ref = cref.ssd_ref_bwd_c(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy, d_final=dfin,
+                             col_block=64)
+    errs = {k: F.rel_err(got[k].float().cpu(), ref[k]) for k in KEYS}
+    errs["dd_init"] = dd_init_err(float(got["dd_init"].cpu()), ref)
+    print("bwd layer full " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= BWD_TOL[torch.bfloat16], (k, v)
+
+
+@pytest.mark.parametrize("rev", [False, True])
+def test_bwd_bidir_workload_sampled_heads(ssd, rev):
+    """The 1,048,576-token bidirectional workload (8 heads x headdim 192,
+    d_state 64), one direction per case, y and dy as halves of
+    [1, L, 8, 384] buffers: a chunk-state workspace past 2^31 bytes and
+    16384-chunk walks.  dx, d d_raw and the initial-state gradient of two
+    heads, every column, against the C adjoint oracle (heads are
+    independent; dB and dC sum over every head, so they are not compared)."""
+    w = WORKLOADS[5]
+    d = make_inputs_device(w, DEV)
+    b, L, H, P = d["x"].shape
+    ycat, _ = ssd.ssd_fwd_bidir(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"])
+    gen = torch.Generator(device=DEV).manual_seed(29)
+    dycat = torch.randn((b, L, H, 2 * P), generator=gen, device=DEV).to(torch.bfloat16)
+    dfin = torch.randn((1, H, w.d_state, P), generator=gen, device=DEV)
+    half = slice(P, 2 * P) if rev else slice(0, P)
+    call = ssd.prepare_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], ycat[..., half],
+                           dycat[..., half], reverse=rev, d_final=dfin)
+    assert call.workspace.numel() > (1 << 31)
+    got = call.run()
+    torch.cuda.synchronize()
+    heads = [1, 6]
+    host = lambda t: t.float().cpu().contiguous()
+    ref = cref.ssd_ref_bwd_c(host(d["x"][:, :, heads]), host(d["d_raw"][:, :, heads]),
+                             d["d_init"], host(d["B"]), host(d["C"]),
+                             host(dycat[..., half][:, :, heads]),
+                             d_final=host(dfin[:, heads]), reverse=rev,
+                             want=("dx", "dd_raw", "dinit_state"), col_block=8)
+    errs = {"dx": F.rel_err(host(got["dx"][:, :, heads]), ref["dx"]),
+            "dd_raw": F.rel_err(host(got["dd_raw"][:, :, heads]), ref["dd_raw"]),
+            "dinit_state": F.rel_err(host(got["dinit_state"][:, heads]), ref["dinit_state"])}
+    print(f"bwd bidir 1M rev={rev} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for k, v in errs.items():
+        assert v <= BWD_TOL[torch.bfloat16], (k, v)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_projection_views(ssd, reverse):
+    """x, B, C and d_raw as views of one [b, L, H*P + 2*G*N + H] projection
+    buffer; the gradients go straight into the same places of a gradient
+    buffer of that layout (each gradient is written with its input's
+    strides); against the adjoint oracle on contiguous copies."""
+    # H = 8 keeps a projection row a whole number of 16-byte units; d_init
+    # is the workloads' (strong decay is test_bwd_dd_raw_strong_decay's case)
+    p = random_problem(361, 2, 300, 8, 64, 64, ngroups=2, dtype="bf16", init_scale=0.5,
+                       d_init=-4.6)
+    b, L, H, P = p["x"].shape
+    G, N = p["B"].shape[2], p["B"].shape[3]
+    W = H * P + 2 * G * N + H
+    proj = torch.empty((b, L, W), dtype=torch.bfloat16)
+    proj[..., :H * P] = p["x"].reshape(b, L, H * P)
+    proj[..., H * P:H * P + G * N] = p["B"].reshape(b, L, G * N)
+    proj[..., H * P + G * N:H * P + 2 * G * N] = p["C"].reshape(b, L, G * N)
+    proj[..., H * P + 2 * G * N:] = p["d_raw"]
+    proj = proj.to(DEV)
+
+    def views(t):
+        return (t[..., :H * P].view(b, L, H, P), t[..., H * P + 2 * G * N:],
+                t[..., H * P:H * P + G * N].view(b, L, G, N),
+                t[..., H * P + G * N:H * P + 2 * G * N].view(b, L, G, N))
+
+    x, dr, Bv, Cv = views(proj)
+    init = p["init_state"].to(DEV)
+    y, _ = ssd.ssd_fwd(x, dr, p["d_init"], Bv, Cv, init_state=init, reverse=reverse)
+    g = torch.Generator().manual_seed(13)
+    dy = torch.randn((b, L, H, P), generator=g).to(torch.bfloat16)
+    dfin = torch.randn((b, H, N, P), generator=g)
+    dproj = torch.full((b, L, W), 9.0, dtype=torch.bfloat16, device=DEV)
+    gx, gdr, gB, gC = views(dproj)
+    got = ssd.ssd_bwd(x, dr, p["d_init"], Bv, Cv, y, _dev(dy), init_state=init, reverse=reverse,
+                      d_final=_dev(dfin), grads={"dx": gx, "dd_raw": gdr, "dB": gB, "dC": gC})
+    # the same call on contiguous copies: only addresses differ, so every
+    # gradient must agree bit for bit
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    yc, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=init,
+                        reverse=reverse)
+    con = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], yc, _dev(dy),
+                      init_state=init, reverse=reverse, d_final=_dev(dfin))
+    torch.cuda.synchronize()
+    assert torch.equal(y, yc)
+    for k, v in (("dx", gx), ("dd_raw", gdr), ("dB", gB), ("dC", gC),
+                 ("dinit_state", got["dinit_state"]), ("dd_init", got["dd_init"])):
+        assert torch.equal(v, con[k]), k
+    assert got["dx"].data_ptr() == gx.data_ptr()
+    ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                        init_state=p["init_state"], d_final=dfin, reverse=reverse)
+    errs = {"dx": F.rel_err(gx.float().cpu(), ref["dx"]),
+            "dd_raw": F.rel_err(gdr.float().cpu(), ref["dd_raw"]),
+            "dB": F.rel_err(gB.float().cpu(), ref["dB"]),
+            "dC": F.rel_err(gC.float().cpu(), ref["dC"]),
+            "dinit_state": F.rel_err(got["dinit_state"].cpu(), ref["dinit_state"])}
+    print(f"bwd projection rev={reverse} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for k, v in errs.items():
+        assert v <= BWD_TOL[torch.bfloat16], (k, v)
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "d d_raw precision at strong decay: the gradient kernel forms the log-decay "
+    "gradient from a chunk-local identity whose per-token terms (dy.y - d dw) are "
+    "much larger than the result, so their bf16 rounding adds up over the chunk "
+    "(1.28e-2 measured on this problem, reverse direction)"))
+def test_bwd_dd_raw_strong_decay(ssd):
+    """Step sizes around 0.2 (d_init -2): the d d_raw bound on the problem
+    whose reverse direction first showed the precision limit."""
+    p = random_problem(361, 2, 300, 8, 64, 64, ngroups=2, dtype="bf16", init_scale=0.5,
+                       d_init=-2.0)
+    d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+    b, L, H, P = p["x"].shape
+    N = p["B"].shape[3]
+    y, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                       init_state=d["init_state"], reverse=True)
+    g = torch.Generator().manual_seed(13)
+    dy = torch.randn((b, L, H, P), generator=g).to(torch.bfloat16)
+    dfin = torch.randn((b, H, N, P), generator=g)
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, _dev(dy),
+                      init_state=d["init_state"], reverse=True, d_final=_dev(dfin))
+    torch.cuda.synchronize()
+    ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
+                        init_state=p["init_state"], d_final=dfin, reverse=True)
+    err = F.rel_err(got["dd_raw"].float().cpu(), ref["dd_raw"])
+    print(f"bwd strong decay rev dd_raw={err:.2e}", flush=True)
+    assert err <= BWD_TOL[torch.bfloat16]

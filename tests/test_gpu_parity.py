@@ -50,9 +50,9 @@ def oracle(p, reverse=False):
                               p["init_state"], p["cu_seqlens"], reverse=reverse)
 
 
-def check(ssd, p, reverse=False, label=""):
+def check(ssd, p, reverse=False, label="", tuning=None):
     tol = TOL[p["x"].dtype]
-    y, f = run(ssd, p, reverse)
+    y, f = run(ssd, p, reverse, tuning=tuning)
     yr, fr = oracle(p, reverse)
     ey, ef = O.rel_err(y, yr), O.rel_err(f, fr)
     print(f"{label} y_err={ey:.3e} final_err={ef:.3e} tol={tol}", flush=True)
@@ -69,18 +69,15 @@ def test_workload_full(ssd, cfg):
     check(ssd, make_inputs(w), label=w.name)
 
 
-def test_workload_varlen_sampled_heads(ssd):
+def test_workload_varlen_full(ssd):
+    """16 packed sequences, 65536 tokens, every head and column against the
+    C oracle."""
     w = WORKLOADS[4]
     p = make_inputs(w)
-    y, f = run(ssd, p)
-    heads = [0, 7, 13, 23]
-    q = dict(p)
-    q["x"] = p["x"][:, :, heads].contiguous()
-    q["d_raw"] = p["d_raw"][:, :, heads].contiguous()
-    yr, fr = oracle(q)
-    ey, ef = O.rel_err(y[:, :, heads], yr), O.rel_err(f[:, heads], fr)
-    print(f"varlen y_err={ey:.3e} final_err={ef:.3e}", flush=True)
-    assert ey <= 1e-2 and ef <= 1e-2
+    d = to_dev(p)
+    plan = ssd.ssd_fwd_plan(ssd.dims_for(d["x"], d["B"], cu_seqlens=d["cu_seqlens"]))
+    assert plan.head_wave == 1 and plan.heads_per_wg == 4   # every slot of the 4-head workgroups
+    check(ssd, p, label="varlen full")
 
 
 def test_workload_bidir_sampled_columns(ssd):
@@ -127,18 +124,19 @@ SHAPES = [
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("reverse", [False, True])
-def test_shapes(ssd, shape, dtype, reverse, family, monkeypatch):
+def test_shapes(ssd, shape, dtype, reverse, family):
     """Every shape through the default kernels, through the span kernels
     alone and with the head-wave kernels forced (they take bf16 problems
     with d_state 64 / 128; others keep the span kernels)."""
     b, L, H, P, N, G = shape
     if dtype == "f32" and N > 128:
         pytest.skip("fp32 path is built for d_state <= 128")
-    if family != "default":
-        monkeypatch.setenv("SSD_KERNEL", family)
+    tuning = None
+    if family == "span" or (family == "hw" and dtype == "bf16" and N in (64, 128)):
+        tuning = {"kernel": family}
     p = random_problem(101, b, L, H, P, N, ngroups=G, dtype=dtype, init_scale=0.5,
                        d_init=-2.0)
-    check(ssd, p, reverse, label=f"{shape} {dtype} rev={reverse} {family}")
+    check(ssd, p, reverse, label=f"{shape} {dtype} rev={reverse} {family}", tuning=tuning)
 
 
 HW_SHAPES = [
@@ -154,82 +152,75 @@ HW_SHAPES = [
 @pytest.mark.parametrize("npb", ["2", "4"])
 @pytest.mark.parametrize("k", ["1", "3", "8"])
 @pytest.mark.parametrize("shape", HW_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_head_wave_variants(ssd, shape, heads, npb, k, monkeypatch):
+def test_head_wave_variants(ssd, shape, heads, npb, k):
     """Every head-wave workgroup shape (1 / 2 / 4 heads, waves of 64 or 32
     headdim columns) at several span lengths, forward and reverse, with a
     partial column group (headdim 80) and two B / C groups."""
-    monkeypatch.setenv("SSD_KERNEL", "hw")
-    monkeypatch.setenv("SSD_HW_HEADS", heads)
-    monkeypatch.setenv("SSD_HW_NPB", npb)
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", k)
     b, L, H, P, N, G = shape
     if npb == "4" and N > 64:
         pytest.skip("full-width head waves are built for d_state <= 64")
+    hs = min(int(heads), 2)  # the state workgroup takes at most two heads
+    tuning = {"kernel": "hw", "heads_scan": int(heads), "heads_state": hs,
+              "cols_per_wave": 16 * int(npb), "chunks_per_span": int(k)}
     p = random_problem(211, b, L, H, P, N, ngroups=G, dtype="bf16", init_scale=0.5)
     d = to_dev(p)
     call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
-    plan = ssd.ssd_fwd_plan(call.dims)
+    plan = ssd.ssd_fwd_plan(call.dims, tuning)
     assert plan.head_wave == 1 and plan.heads_per_wg == int(heads)
     assert plan.cols_per_wave == 16 * int(npb) and plan.chunks_per_span == int(k)
     for rev in (False, True):
-        check(ssd, p, rev, label=f"hw {shape} hg={heads} npb={npb} K={k} rev={rev}")
+        check(ssd, p, rev, label=f"hw {shape} hg={heads} npb={npb} K={k} rev={rev}", tuning=tuning)
 
 
 @pytest.mark.parametrize("d_init", [-9.0, -3.0, 1.0])
 @pytest.mark.parametrize("N", [64, 128])
-def test_head_wave_rescaled_state(ssd, d_init, N, monkeypatch):
+def test_head_wave_rescaled_state(ssd, d_init, N):
     """The rescaled state across long spans: weak decay (no restart in 16
     chunks), medium decay (the running scale restarts every few chunks) and
     strong decay (every chunk restarts), forward and reverse."""
-    monkeypatch.setenv("SSD_KERNEL", "hw")
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "16")
+    tuning = {"kernel": "hw", "chunks_per_span": 16}
     p = random_problem(227, 1, 1500, 4, 64, N, dtype="bf16", init_scale=0.5, d_init=d_init,
                        d_raw_scale=2.0)
     for rev in (False, True):
-        check(ssd, p, rev, label=f"hw rescale d_init={d_init} N={N} rev={rev}")
+        check(ssd, p, rev, label=f"hw rescale d_init={d_init} N={N} rev={rev}", tuning=tuning)
 
 
 @pytest.mark.parametrize("npb", ["2", "4"])
-def test_head_wave_varlen(ssd, npb, monkeypatch):
-    monkeypatch.setenv("SSD_KERNEL", "hw")
-    monkeypatch.setenv("SSD_HW_NPB", npb)
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+def test_head_wave_varlen(ssd, npb):
+    N = 64 if npb == "4" else 128  # full-width waves are built for d_state 64
+    tuning = {"kernel": "hw", "cols_per_wave": 16 * int(npb), "chunks_per_span": 2}
     lens = [1, 63, 64, 65, 0, 200, 129, 7, 0, 640]
-    p = random_problem(223, 1, 0, 4, 64, 128, dtype="bf16", lengths=lens, init_scale=0.3)
+    p = random_problem(223, 1, 0, 4, 64, N, dtype="bf16", lengths=lens, init_scale=0.3)
     for rev in (False, True):
-        check(ssd, p, rev, label=f"hw varlen npb={npb} rev={rev}")
+        check(ssd, p, rev, label=f"hw varlen npb={npb} rev={rev}", tuning=tuning)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("reverse", [False, True])
-def test_shapes_fused_launch(ssd, shape, dtype, reverse, monkeypatch):
+def test_shapes_fused_launch(ssd, shape, dtype, reverse):
     """The single fused launch, one chunk per span (so every sequence longer
     than 64 tokens hands states between workgroups), on every shape."""
-    monkeypatch.setenv("SSD_KERNEL", "span")
     b, L, H, P, N, G = shape
     if dtype == "f32" and N > 128:
         pytest.skip("fp32 path is built for d_state <= 128")
     if (L + 63) // 64 > 16:
         pytest.skip("more than 16 spans per sequence")
-    monkeypatch.setenv("SSD_FUSE_PASS", "2")
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "1")
+    tuning = {"kernel": "span", "state_pass": "fused", "chunks_per_span": 1}
     p = random_problem(103, b, L, H, P, N, ngroups=G, dtype=dtype, init_scale=0.5,
                        d_init=-2.0)
-    check(ssd, p, reverse, label=f"fused {shape} {dtype} rev={reverse}")
+    check(ssd, p, reverse, label=f"fused {shape} {dtype} rev={reverse}", tuning=tuning)
 
 
 @pytest.mark.parametrize("fuse", ["1", "2"])
-def test_two_heads_per_scan_workgroup(ssd, fuse, monkeypatch):
+def test_two_heads_per_scan_workgroup(ssd, fuse):
     """Span workgroups carrying two heads (one quad of waves each) in the
     folding and the fused plans."""
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    monkeypatch.setenv("SSD_FUSE_PASS", fuse)
-    monkeypatch.setenv("SSD_HEADS_SCAN", "2")
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+    tuning = {"kernel": "span", "state_pass": int(fuse) + 1, "heads_scan": 2,
+              "heads_state": 2, "chunks_per_span": 2}
     p = random_problem(107, 2, 700, 4, 64, 64, dtype="bf16", init_scale=0.5)
-    check(ssd, p, False, label=f"hg2 fuse={fuse}")
-    check(ssd, p, True, label=f"hg2 fuse={fuse} rev")
+    check(ssd, p, False, label=f"hg2 fuse={fuse}", tuning=tuning)
+    check(ssd, p, True, label=f"hg2 fuse={fuse} rev", tuning=tuning)
 
 
 @pytest.mark.parametrize("reverse", [False, True])
@@ -257,46 +248,43 @@ def test_weak_decay_long_memory(ssd):
 
 
 @pytest.mark.parametrize("k", ["1", "2", "3", "8", "64"])
-def test_span_length_invariance(ssd, k, monkeypatch):
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", k)
+def test_span_length_invariance(ssd, k):
+    tuning = {"chunks_per_span": int(k)}
     p = random_problem(127, 2, 777, 3, 64, 128, dtype="bf16", init_scale=0.5)
-    check(ssd, p, False, label=f"K={k}")
+    check(ssd, p, False, label=f"K={k}", tuning=tuning)
     lens = [100, 700, 1, 333]
     q = random_problem(131, 1, 0, 2, 64, 64, dtype="f32", lengths=lens, init_scale=0.5)
-    check(ssd, q, True, label=f"K={k} varlen rev f32")
+    check(ssd, q, True, label=f"K={k} varlen rev f32", tuning=tuning)
 
 
 @pytest.mark.parametrize("fuse", ["0", "1", "2"])
 @pytest.mark.parametrize("reverse", [False, True])
-def test_state_pass_folded_or_separate(ssd, fuse, reverse, monkeypatch):
+def test_state_pass_folded_or_separate(ssd, fuse, reverse):
     """Every way of handing the state from span to span matches the oracle:
     the separate state_pass kernel (0), span_scan folding the earlier span
     states of its sequence itself (1), and the single fused launch whose
     workgroups hand span states to each other (2)."""
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    monkeypatch.setenv("SSD_FUSE_PASS", fuse)
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "2")
+    tuning = {"kernel": "span", "state_pass": int(fuse) + 1, "chunks_per_span": 2}
     p = random_problem(151, 2, 1000, 3, 64, 128, dtype="bf16", init_scale=0.5)
     d = to_dev(p)
     call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
-    assert ssd.ssd_fwd_plan(call.dims).fused_pass == int(fuse)
-    check(ssd, p, reverse, label=f"fuse={fuse} bf16")
+    assert ssd.ssd_fwd_plan(call.dims, tuning).fused_pass == int(fuse)
+    check(ssd, p, reverse, label=f"fuse={fuse} bf16", tuning=tuning)
     q = random_problem(157, 3, 500, 2, 32, 64, dtype="f32", init_scale=0.5)
-    check(ssd, q, reverse, label=f"fuse={fuse} f32")
+    check(ssd, q, reverse, label=f"fuse={fuse} f32", tuning=tuning)
 
 
-def test_state_pass_long_walks(ssd, monkeypatch):
+def test_state_pass_long_walks(ssd):
     """The separate state pass over walks of 1 to 38 spans (one chunk each):
     every position of its two batches of eight in flight, the tail of a walk
     inside either batch, and walks longer than two batches; weak decay, so a
     state carried or dropped wrongly anywhere along a walk shows at its end."""
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    monkeypatch.setenv("SSD_SPAN_CHUNKS", "1")
+    tuning = {"kernel": "span", "chunks_per_span": 1}
     lens = [64 * 37 + 5, 64 * 16, 64 * 17 - 3, 64 * 8, 64 * 9, 1, 64 * 24 + 1]
     p = random_problem(173, 1, 0, 2, 16, 16, dtype="f32", lengths=lens, d_init=-6.0,
                        init_scale=1.0)
-    check(ssd, p, False, label="long walks")
-    check(ssd, p, True, label="long walks rev")
+    check(ssd, p, False, label="long walks", tuning=tuning)
+    check(ssd, p, True, label="long walks rev", tuning=tuning)
 
 
 def _sync_words(ws, chains):
@@ -307,28 +295,28 @@ def _sync_words(ws, chains):
     return timeouts, [tuple(w) for w in words]
 
 
-def test_fused_handoff_repeated_calls(ssd, monkeypatch):
+FUSED = {"kernel": "span", "state_pass": "fused"}
+
+
+def test_fused_handoff_repeated_calls(ssd):
     """The fused launch hands span states between workgroups through the
-    workspace, with flags tagged by a per-launch epoch.  Alternate two input
+    workspace, with flags it resets before every launch.  Alternate two input
     sets on one workspace: every call must reproduce its input set's first
     result bit for bit (a state left by the other set's call would change
     it), agree with the three-launch plan, and leave every chain's word at
-    count 0, epoch = number of fused launches, with no timed-out waits.
-    1024 workgroups of 16 spans per sequence: more than the GPU holds at
-    once."""
-    monkeypatch.setenv("SSD_KERNEL", "span")
-    monkeypatch.delenv("SSD_SPAN_CHUNKS", raising=False)
-    monkeypatch.setenv("SSD_FUSE_PASS", "2")
+    count 0, epoch 1, with no timed-out waits.  1024 workgroups of 16 spans
+    per sequence: more than the GPU holds at once."""
     probs = [random_problem(seed, 8, 4096, 8, 64, 128, dtype="bf16", init_scale=0.5)
              for seed in (161, 163)]
     devs = [to_dev(p) for p in probs]
-    calls = [ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
-             for d in devs]
-    plan = ssd.ssd_fwd_plan(calls[0].dims)
+    calls = [ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"],
+                         tuning=FUSED) for d in devs]
+    plan = ssd.ssd_fwd_plan(calls[0].dims, FUSED)
     assert plan.fused_pass == 2 and plan.nspan == 8 * 16
     ws = calls[0].workspace
+    ws.fill_(0xA5)  # no initialization is needed: start from garbage
     calls = [ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"],
-                         workspace=ws) for d in devs]
+                         workspace=ws, tuning=FUSED) for d in devs]
     first = []
     for i in range(24):
         y, f = calls[i % 2].run()
@@ -339,14 +327,40 @@ def test_fused_handoff_repeated_calls(ssd, monkeypatch):
             y0, f0 = first[i % 2]
             assert torch.equal(y, y0) and torch.equal(f, f0), f"call {i} differs from call {i % 2}"
     torch.cuda.synchronize()
-    assert _sync_words(ws, 8 * 8) == (0, [(0, 24)] * 64)
-    monkeypatch.setenv("SSD_FUSE_PASS", "0")
+    assert _sync_words(ws, 8 * 8) == (0, [(0, 1)] * 64)
     for k, d in enumerate(devs):
-        y3, f3 = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+        y3, f3 = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                             init_state=d["init_state"], tuning={"kernel": "span", "state_pass": "pass"})
         torch.cuda.synchronize()
         y0, f0 = first[k]
         assert O.rel_err(y0.float().cpu(), y3.float().cpu()) <= 1e-2
         assert O.rel_err(f0.cpu(), f3.cpu()) <= 1e-2
+
+
+def test_fused_after_other_plans_and_sizes(ssd):
+    """A fused call right after calls of other plans and other sizes on the
+    same workspace (their span states sit where the fused words go): each
+    fused call matches the oracle and no flag wait runs out."""
+    big = random_problem(181, 2, 1000, 4, 64, 128, dtype="bf16", init_scale=0.5)
+    small = random_problem(191, 1, 300, 2, 64, 64, dtype="bf16", init_scale=0.5)
+    packed = random_problem(193, 1, 0, 4, 64, 128, dtype="bf16", lengths=[500, 1, 700],
+                            init_scale=0.5)
+    need = max(ssd.ssd_fwd_plan(ssd.dims_for(to_dev(q)["x"], to_dev(q)["B"], cu_seqlens=(
+        None if q["cu_seqlens"] is None else to_dev(q)["cu_seqlens"])), t).workspace_bytes
+               for q, t in ((big, FUSED), (small, FUSED), (packed, None), (big, None)))
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV)
+    order = [(packed, None), (big, FUSED), (big, None), (small, FUSED), (big, FUSED),
+             (packed, None), (small, FUSED)]
+    for q, t in order:
+        d = to_dev(q)
+        y, f = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                           init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], workspace=ws,
+                           tuning=t)
+        torch.cuda.synchronize()
+        yr, fr = oracle(q)
+        assert O.rel_err(y.float().cpu(), yr) <= 1e-2 and O.rel_err(f.cpu(), fr) <= 1e-2
+        if t is FUSED:
+            assert int(ws[8:12].view(torch.int32).item()) == 0
 
 
 def test_empty_sequence_keeps_init(ssd):
@@ -373,3 +387,110 @@ def test_bidir_matches_two_calls(ssd):
     assert torch.equal(y[..., :32], yf) and torch.equal(y[..., 32:], yr)
     yo, _ = oracle(p, True)
     assert O.rel_err(yr.float().cpu(), yo) <= 1e-2
+
+
+# ------------------------------------------------------------ boundary
+def test_ssd_check_rejects_bad_cu_seqlens(ssd, monkeypatch):
+    """With SSD_CHECK=1 the library copies cu_seqlens to the host and
+    returns SSD_ERR_CU_SEQLENS for a non-monotone one or one that does not
+    end at L, launching nothing: sentinel-filled outputs stay as they were."""
+    monkeypatch.setenv("SSD_CHECK", "1")
+    p = random_problem(197, 1, 0, 2, 64, 64, dtype="bf16", lengths=[100, 50, 50])
+    d = to_dev(p)
+    L = d["x"].shape[1]
+    for bad in ([0, 100, 50, 200], [0, 100, 150, 180], [5, 100, 150, 200]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        y = torch.full_like(d["x"], 7.0)
+        fin = torch.full((3, 2, 64, 64), -3.0, device=DEV)
+        with pytest.raises(ssd.SsdError) as e:
+            ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], cu_seqlens=cu, y=y,
+                        final_state=fin)
+        assert e.value.status == -8
+        torch.cuda.synchronize()
+        assert bool((y == 7.0).all()) and bool((fin == -3.0).all())
+    assert L == 200
+    # a valid one passes the check and matches the oracle
+    check(ssd, p, label="checked cu_seqlens")
+
+
+@pytest.mark.parametrize("plan", [None, "fold", "fused"])
+def test_final_state_in_place(ssd, plan):
+    """final_state written over init_state (one buffer): the library takes
+    the separate pass, which reads each entry before writing it; the result
+    matches the oracle run from the original initial state.  Eight spans
+    per sequence, so the fold would otherwise read init_state in every
+    span's workgroup."""
+    p = random_problem(199, 2, 2048, 4, 64, 128, dtype="bf16", init_scale=0.5)
+    d = to_dev(p)
+    tuning = None if plan is None else {"kernel": "span", "state_pass": plan}
+    info = ssd.ssd_fwd_plan(ssd.dims_for(d["x"], d["B"]), tuning)
+    assert info.fused_pass == {None: 1, "fold": 1, "fused": 2}[plan] and info.nspan == 16
+    st = d["init_state"].clone()
+    y, f = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=st,
+                       final_state=st, tuning=tuning)
+    torch.cuda.synchronize()
+    assert f.data_ptr() == st.data_ptr()
+    yr, fr = oracle(p)
+    assert O.rel_err(y.float().cpu(), yr) <= 1e-2 and O.rel_err(st.cpu(), fr) <= 1e-2
+
+
+def projection(p, dev=DEV):
+    """x, B, C and d_raw as views of one [b, L, H*P + 2*G*N + H] buffer (the
+    output of one linear map of the input), filled with the problem's
+    values."""
+    b, L, H, P = p["x"].shape
+    G, N = p["B"].shape[2], p["B"].shape[3]
+    W = H * P + 2 * G * N + H
+    proj = torch.empty((b, L, W), dtype=p["x"].dtype)
+    proj[..., :H * P] = p["x"].reshape(b, L, H * P)
+    proj[..., H * P:H * P + G * N] = p["B"].reshape(b, L, G * N)
+    proj[..., H * P + G * N:H * P + 2 * G * N] = p["C"].reshape(b, L, G * N)
+    proj[..., H * P + 2 * G * N:] = p["d_raw"]
+    proj = proj.to(dev)
+    views = {"x": proj[..., :H * P].view(b, L, H, P),
+             "B": proj[..., H * P:H * P + G * N].view(b, L, G, N),
+             "C": proj[..., H * P + G * N:H * P + 2 * G * N].view(b, L, G, N),
+             "d_raw": proj[..., H * P + 2 * G * N:]}
+    return proj, views
+
+
+@pytest.mark.parametrize("tuning", [None, {"kernel": "hw"}, {"kernel": "span", "state_pass": "fused"},
+                                    {"kernel": "span", "state_pass": "pass"}, {"state_f32": 1}],
+                         ids=["default", "hw", "fused", "pass", "f32states"])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_projection_views(ssd, tuning, reverse):
+    """x, B, C and d_raw read through the strides of one projection buffer
+    ([b, L, H*P + 2*G*N + H]), y written into the second half of a
+    [b, L, H, 2P] buffer; against the oracle on contiguous copies."""
+    # H = 8 keeps a projection row (H*P + 2*G*N + H bf16 values) a whole
+    # number of 16-byte units, as the strides of x, B and C must be
+    p = random_problem(211, 2, 700, 8, 64, 128, dtype="bf16", init_scale=0.5)
+    proj, v = projection(p)
+    b, L, H, P = p["x"].shape
+    ycat = torch.zeros((b, L, H, 2 * P), dtype=torch.bfloat16, device=DEV)
+    d_init_state = p["init_state"].to(DEV)
+    y, f = ssd.ssd_fwd(v["x"], v["d_raw"], p["d_init"], v["B"], v["C"], init_state=d_init_state,
+                       reverse=reverse, y=ycat[..., P:], tuning=tuning)
+    torch.cuda.synchronize()
+    yr, fr = oracle(p, reverse)
+    ey, ef = O.rel_err(y.float().cpu(), yr), O.rel_err(f.cpu(), fr)
+    print(f"projection {tuning} rev={reverse} y_err={ey:.3e} final_err={ef:.3e}", flush=True)
+    assert ey <= 1e-2 and ef <= 1e-2
+    assert bool((ycat[..., :P] == 0).all())
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_state_f32_option(ssd, cfg):
+    """Span states kept in float32 for bf16 inputs (the uncompressed
+    reference point of 16-bit state storage): same bound, and the error
+    against the oracle of both options is printed."""
+    w = WORKLOADS[cfg]
+    p = make_inputs(w)
+    yr, fr = oracle(p)
+    errs = {}
+    for opt in (0, 1):
+        y, f = run(ssd, p, tuning={"kernel": "span", "state_f32": opt})
+        errs[opt] = (O.rel_err(y, yr), O.rel_err(f, fr))
+        assert max(errs[opt]) <= 1e-2
+    print(f"{w.name} bf16 states y/final err {errs[0][0]:.3e}/{errs[0][1]:.3e}, "
+          f"f32 states {errs[1][0]:.3e}/{errs[1][1]:.3e}", flush=True)
