@@ -30,7 +30,9 @@
  * with separate workspaces may run concurrently.  All argument checks run
  * on the host before any launch; on an error status nothing is launched and
  * no output is written.  The library reads one environment variable,
- * SSD_CHECK; its tuning choices are explicit arguments (ssd_tuning).
+ * SSD_CHECK; its tuning choices are explicit arguments (ssd_tuning).  (The
+ * one exception to "no global state" is ssd_fwd_noalloc's per-device
+ * scratch array and the address it caches for each device.)
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -58,9 +60,11 @@ enum {
     SSD_ERR_HIP = -7,             /* a HIP launch or runtime call failed         */
     SSD_ERR_CU_SEQLENS = -8,      /* cu_seqlens invalid (checked only when the
                                      environment sets SSD_CHECK=1)               */
-    SSD_ERR_OVERLAP = -9          /* init_state and final_state (or d_final and
+    SSD_ERR_OVERLAP = -9,         /* init_state and final_state (or d_final and
                                      dinit_state) overlap without being the
                                      same buffer                                */
+    SSD_ERR_SCRATCH = -10         /* ssd_fwd_noalloc: the sizes need more
+                                     scratch than its fixed buffer holds       */
 };
 
 /* Element type of x, d_raw, B, C and y.  States are always float32. */
@@ -303,6 +307,31 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
                float* dinit_state, float* dd_init,
                void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * ssd_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same scan with the planner's choices, its scratch taken from a fixed
+ * array inside the library instead of a workspace argument.  Each GPU the
+ * library runs on holds one such array of ssd_fwd_noalloc_max_bytes()
+ * bytes (64 MiB) until the process ends; its device address is looked up
+ * once per device, on the first call with that device current.  The call
+ * allocates nothing and synchronizes nothing (SSD_CHECK=1 aside).
+ * Arguments as ssd_fwd without the workspace.  Sizes whose workspace
+ * (ssd_fwd_workspace_bytes) exceeds the array return SSD_ERR_SCRATCH before
+ * any HIP call.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap in time on one GPU (different streams, or threads) race and
+ * give unspecified results; nothing in the array needs to start at zero.
+ */
+int ssd_fwd_noalloc(const ssd_dims* dims, const ssd_layout* layout,
+                    const void* x, const void* d_raw, float d_init,
+                    const void* B, const void* C,
+                    const float* init_state, const int32_t* cu_seqlens, int32_t reverse,
+                    void* y, float* final_state,
+                    void* stream);
+
+/* Bytes of ssd_fwd_noalloc's fixed scratch array on each GPU. */
+size_t ssd_fwd_noalloc_max_bytes(void);
 
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(int status);

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     CHUNK, SSD_BF16, SSD_F32, STAGE_ALL, STAGE_PASS, STAGE_SCAN, STAGE_STATE, STAGE_TABLE,
     TUNING_FIELDS, PreparedBwd, PreparedCall, SsdDims, SsdError, SsdLayout, SsdPlanInfo,
     SsdTuning, dims_for, layout_of, library, make_dims, make_tuning, prepare, prepare_bwd,
-    ssd_abi_version, ssd_bwd, ssd_bwd_workspace_bytes, ssd_fwd, ssd_fwd_bidir, ssd_fwd_plan,
+    ssd_abi_version, ssd_bwd, ssd_bwd_workspace_bytes, ssd_fwd, ssd_fwd_bidir, ssd_fwd_noalloc,
+    ssd_fwd_noalloc_max_bytes, ssd_fwd_plan,
     ssd_fwd_workspace_bytes, ssd_status_string,
 )

@@ -152,6 +152,10 @@ def library() -> ctypes.CDLL:
         lib.ssd_bwd.argtypes = bwd_args
         lib.ssd_bwd_ex.restype = ctypes.c_int
         lib.ssd_bwd_ex.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(SsdTuning)] + bwd_args[1:]
+        lib.ssd_fwd_noalloc.restype = ctypes.c_int
+        lib.ssd_fwd_noalloc.argtypes = fwd_args[:11] + [P_]
+        lib.ssd_fwd_noalloc_max_bytes.restype = ctypes.c_size_t
+        lib.ssd_fwd_noalloc_max_bytes.argtypes = []
         _lib = lib
     return _lib
 
@@ -334,6 +338,30 @@ def prepare(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None, cu_seqlen
             _ptr(workspace), workspace.numel())
     keep = (x, d_raw, B, C, init_state, cu_seqlens)
     return PreparedCall(dims, tun, lay, args, keep, y, final_state, workspace)
+
+
+def ssd_fwd_noalloc(x, d_raw, d_init, B, C, y, final_state=None, init_state=None,
+                    cu_seqlens=None, reverse=False):
+    """ssd_fwd_noalloc: the forward scan with the library's fixed per-GPU
+    scratch instead of a workspace.  y (and final_state, if wanted) are the
+    caller's preallocated outputs; nothing is allocated.  Returns (y,
+    final_state)."""
+    b, L, H, P = x.shape
+    dims = dims_for(x, B, CHUNK, cu_seqlens)
+    lay = layout_of(x, d_raw, B, C, y)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = library().ssd_fwd_noalloc(
+            ctypes.byref(dims), ctypes.byref(lay), _ptr(x), _ptr(d_raw), float(d_init), _ptr(B),
+            _ptr(C), _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0, _ptr(y),
+            _ptr(final_state), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise SsdError(rc, "ssd_fwd_noalloc")
+    return y, final_state
+
+
+def ssd_fwd_noalloc_max_bytes() -> int:
+    return int(library().ssd_fwd_noalloc_max_bytes())
 
 
 def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,

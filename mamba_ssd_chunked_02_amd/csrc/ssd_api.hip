@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/ssd.h"
@@ -338,6 +339,30 @@ int check_cu(const int32_t* cu, int32_t nseq, int64_t T, hipStream_t s) {
     return SSD_OK;
 }
 
+// ssd_fwd_noalloc's scratch: what ssd_fwd takes from its workspace (the
+// header, span states and decays, and the varlen span table) in one fixed
+// device array.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code its name is only a stand-in: the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch array (nullptr on failure).
+void* scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,6 +391,9 @@ const char* ssd_status_string(int status) {
             return "SSD_ERR_CU_SEQLENS: cu_seqlens not 0..L and non-decreasing";
         case SSD_ERR_OVERLAP:
             return "SSD_ERR_OVERLAP: state buffers overlap without being the same buffer";
+        case SSD_ERR_SCRATCH:
+            return "SSD_ERR_SCRATCH: the problem needs more scratch than ssd_fwd_noalloc's "
+                   "fixed buffer (ssd_fwd_noalloc_max_bytes)";
     }
     return "unknown ssd status";
 }
@@ -521,6 +549,24 @@ int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     return SSD_OK;
+}
+
+size_t ssd_fwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int ssd_fwd_noalloc(const ssd_dims* dims, const ssd_layout* layout, const void* x,
+                    const void* d_raw, float d_init, const void* B, const void* C,
+                    const float* init_state, const int32_t* cu_seqlens, int32_t reverse, void* y,
+                    float* final_state, void* stream) {
+    Plan pl;
+    const int st = make_plan(dims, nullptr, &pl);
+    if (st != SSD_OK) return st;
+    if (pl.total > kScratchBytes) return SSD_ERR_SCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    void* ptr = scratch_address(dev);
+    if (!ptr) return SSD_ERR_HIP;
+    return ssd_fwd_ex(SSD_STAGE_ALL, dims, nullptr, layout, x, d_raw, d_init, B, C, init_state,
+                      cu_seqlens, reverse, y, final_state, ptr, kScratchBytes, stream);
 }
 
 size_t ssd_bwd_workspace_bytes(const ssd_dims* dims) {

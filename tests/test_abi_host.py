@@ -373,3 +373,21 @@ def test_bwd_rejects_bad_arguments(m):
     assert call_bwd(m, ok, dfin=FAKE, dinit=FAKE, ws=None) == -6          # same buffer: allowed
     assert call_bwd(m, ok, ws=None) == -6                                  # WORKSPACE
     assert call_bwd(m, ok, wsb=16) == -6
+
+
+def test_noalloc_rejects_sizes_past_its_scratch(m):
+    """ssd_fwd_noalloc refuses sizes whose workspace exceeds its fixed
+    64 MiB array with SSD_ERR_SCRATCH, before any HIP call (NULL pointers:
+    nothing could be launched even if the check were missing)."""
+    assert m.ssd_fwd_noalloc_max_bytes() == 64 << 20
+    big = m.make_dims(1, 1 << 20, 8, 192, 64)
+    assert m.ssd_fwd_workspace_bytes(big) > 64 << 20
+    lay = m.SsdLayout(8 * 192, 192, 8, 1, 64, 64, 64, 64, 8 * 192, 192, 8 * 192, 192)
+    rc = m.library().ssd_fwd_noalloc(ctypes.byref(big), ctypes.byref(lay), None, None, -4.6,
+                                      None, None, None, None, 0, None, None, None)
+    assert rc == -10
+    assert "scratch" in m.ssd_status_string(-10)
+    # the layer, wide and packed workloads fit
+    for d in (m.make_dims(2, 2048, 24, 64, 128), m.make_dims(1, 8192, 80, 64, 128),
+              m.make_dims(1, 65536, 24, 64, 128, nseq=16)):
+        assert m.ssd_fwd_workspace_bytes(d) <= 64 << 20
