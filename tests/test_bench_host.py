@@ -49,3 +49,18 @@ def test_layer_algorithmic_bytes_by_hand():
     assert plan0["scan"] == x + d_raw + 2 * bc + states + x
     fused = bench.stage_bytes(w, _Plan(2), spans)["fused"]
     assert fused == x + d_raw + 2 * bc + x + final + (16 - 2) * 24 * (128 * 64 * 2 + 4)
+
+
+def test_layer_algorithmic_flops_by_hand():
+    """Per token-head: 2NP for the chunk state, 2NP + 65P for the scan's
+    inter- and intra-chunk products; 65N per token for the causal C B^T of
+    the one B/C group; 2NP per span-head for the pair combine."""
+    w = by_name("layer")
+    spans = bench.spans_used(w, _Plan(1))
+    th = 4096 * 24
+    f = bench.stage_flops(w, _Plan(1), spans)
+    assert f["state"] == th * 2 * 128 * 64
+    assert f["scan"] == th * (2 * 128 * 64 + 65 * 64) + 4096 * 65 * 128 + 16 * 24 * 2 * 128 * 64
+    f0 = bench.stage_flops(w, _Plan(0), spans)
+    assert f0["pass"] == 16 * 24 * 2 * 128 * 64
+    assert f0["state"] + f0["pass"] + f0["scan"] == bench.stage_flops(w, _Plan(2), spans)["fused"]
