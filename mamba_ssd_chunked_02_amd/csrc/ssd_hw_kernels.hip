@@ -213,9 +213,21 @@ __device__ __forceinline__ bf16x4 mask_tile_hw(const HwDecay& D, const f32x4& ac
     return v;
 }
 
+// Waves per SIMD the registers allow: two (256 VGPRs) for the half-width
+// state kernels and for the scans of 8-wave workgroups (which need two per
+// SIMD to fit a CU) and of two d_state-64 heads; one (up to 512 VGPRs) for
+// full-width waves and the other half-width scans, whose state, fragments and
+// outputs of 32 columns need more.
+template <int N, int HG, int NPB, int MODE>
+constexpr int hw_occupancy() {
+    if (NPB == 4) return 1;
+    if (MODE == kHwState) return 2;
+    return (HG == 4 || (N == 64 && HG == 2)) ? 2 : 1;
+}
+
 // Head-wave span kernel; see the file comment.
 template <int N, int HG, int NPB, int MODE>
-__global__ __launch_bounds__(64 * HG * (4 / NPB), (NPB == 2 || N <= 64) ? 2 : 1) void hw_span_kernel(
+__global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE>())) void hw_span_kernel(
     KParams p) {
     using Cf = HwCfg<N, HG, NPB>;
     using Sm = HwSmem<N, HG, NPB, MODE == kHwScan>;

@@ -126,14 +126,18 @@ __device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay&
     if constexpr (SCAN) sm.lf[q][lslot(TB, SB >> 1)][SB & 1][lane] = v;
 }
 
-// Register budget: 2 waves per SIMD (256 VGPRs) -- two 4-wave workgroups
-// per CU, or one 8-wave one; lighter variants get more from their natural
-// register use.  A scan with state rows wider than 256 bytes gets 512.
+// Register budget: 2 waves per SIMD (256 VGPRs) where the kernel fits in
+// them -- two 4-wave workgroups per CU, or one 8-wave one (an 8-wave
+// workgroup needs two waves per SIMD to fit a CU at all).  The variants whose
+// fragments and state need more (bf16 d_state 256; fp32 d_state 128 states,
+// fp32 d_state >= 64 scans) get one wave per SIMD and up to 512 VGPRs.
 enum { kModeState = 0, kModeScan = 1, kModeFused = 2, kModeStateGrad = 3 };
 constexpr bool is_state(int mode) { return mode == kModeState || mode == kModeStateGrad; }
 template <typename T, int N, int HG, int MODE>
 constexpr int span_occupancy() {
-    return HG == 1 && !(!is_state(MODE) && N * sizeof(T) > 256) ? 2 : 1;
+    if (HG != 1) return 2;
+    if (sizeof(T) == 2) return N <= 128 ? 2 : 1;
+    return (is_state(MODE) ? N <= 64 : N <= 32) ? 2 : 1;
 }
 
 // Accesses coherent across the whole device (agent scope, all XCDs): the
