@@ -56,9 +56,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "mamba_ssd_chunked_02_amd", "csrc", f)
                for f in ("ssd_kernels.hip", "ssd_device.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_layer.json")
-STAGE_KERNEL = {"state": "span_kernel<bf16, N, 1, kModeState>", "pass": "state_pass_kernel",
-                "scan": "span_kernel<bf16, N, 1, kModeScan>",
-                "fused": "span_kernel<bf16, N, 1, kModeFused>", "table": "span_table_kernel"}
+STAGE_KERNEL = {"state": "span_kernel<{T}, {N}, 1, kModeState>", "pass": "state_pass_kernel<{T}>",
+                "scan": "span_kernel<{T}, {N}, 1, kModeScan>",
+                "fused": "span_kernel<{T}, {N}, 1, kModeFused>", "table": "span_table_kernel"}
 DTYPE_LABEL = {"bf16": "bf16 in, bf16 span states, fp32 accumulation and final state",
                "f32": "fp32 in, fp32 span states and accumulation"}
 CONTEXT = {"pages_tokens_per_s": 950,
@@ -74,7 +74,7 @@ def kernel_label(stage: str, plan, w) -> str:
         heads = plan.heads_per_wg if stage == "scan" else plan.heads_per_state_wg
         return (f"hw_span_kernel<{w.d_state}, {heads}, "
                 f"{plan.cols_per_wave // 16}, {mode}>")
-    return STAGE_KERNEL[stage]
+    return STAGE_KERNEL[stage].format(T="bf16" if w.dtype == "bf16" else "float", N=w.d_state)
 
 
 def kernel_source_hash() -> str:
