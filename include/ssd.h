@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 6
+#define SSD_ABI_VERSION 7
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -265,8 +265,8 @@ int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuni
  * d_state values return SSD_ERR_UNSUPPORTED.  Any headdim ssd_fwd accepts.
  *
  * Arguments as ssd_fwd, plus:
- *   y           the forward output of these inputs (as ssd_fwd wrote it),
- *               strides layout->y_*
+ *   y           not read (the gradients are formed from the inputs and the
+ *               chunk states); may be NULL.  layout->y_* is not checked.
  *   dy          dL/dy, dtype, strides layout->dy_*
  *   d_final     dL/d final_state [S, H, N, P] float32, or NULL for zeros
  *   dx          output, dtype, laid out like x (strides layout->x_*)
@@ -280,7 +280,7 @@ int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuni
  *   workspace   at least ssd_bwd_workspace_bytes(dims) bytes, 256-byte
  *               aligned, no initialization needed; calls that overlap in
  *               time need separate workspaces
- * x, B, C, y, dy, dx, dB and dC must be 16-byte aligned.  The gradients must
+ * x, B, C, dy, dx, dB and dC must be 16-byte aligned.  The gradients must
  * not overlap the inputs.  Outputs for tokens outside every cu_seqlens
  * segment are not written.  Returns SSD_OK once the work is queued.
  */

@@ -427,17 +427,20 @@ def prepare_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size=CHUNK, init_state=None
     workspace when not given.  dx, dd_raw, dB and dC are laid out like x,
     d_raw, B and C (the library writes each gradient with its input's
     strides); ``grads`` may supply some or all of them, e.g. as views of one
-    projection-gradient buffer laid out like the inputs' projection."""
+    projection-gradient buffer laid out like the inputs' projection.  ``y``
+    (the forward output) is optional: the library does not read it."""
     if x.dim() != 4 or d_raw.dim() != 3 or B.dim() != 4 or C.dim() != 4:
         raise ValueError("x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] expected")
     b, L, H, P = x.shape
     dev = x.device
     for name, t in (("d_raw", d_raw), ("B", B), ("C", C), ("y", y), ("dy", dy)):
+        if t is None and name == "y":
+            continue
         if t.device != dev or t.dtype != x.dtype:
             raise ValueError(f"{name} must be on {dev} with dtype {x.dtype}")
     if tuple(d_raw.shape) != (b, L, H) or tuple(B.shape[:2]) != (b, L) or B.shape != C.shape:
         raise ValueError("shape mismatch between x, d_raw, B and C")
-    if tuple(y.shape) != (b, L, H, P) or tuple(dy.shape) != (b, L, H, P):
+    if (y is not None and tuple(y.shape) != (b, L, H, P)) or tuple(dy.shape) != (b, L, H, P):
         raise ValueError("y and dy must have x's shape")
     G, N = B.shape[2], B.shape[3]
     if cu_seqlens is not None:
@@ -471,19 +474,20 @@ def prepare_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size=CHUNK, init_state=None
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args = (_ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
             _ptr(init_state), _ptr(cu_seqlens), 1 if reverse else 0,
-            _ptr(y), _ptr(dy), _ptr(d_final),
+            None, _ptr(dy), _ptr(d_final),
             _ptr(g["dx"]), _ptr(g["dd_raw"]), _ptr(g["dB"]), _ptr(g["dC"]),
             _ptr(g["dinit_state"]), _ptr(g["dd_init"]),
             _ptr(workspace), workspace.numel())
-    keep = (x, d_raw, B, C, y, dy, init_state, cu_seqlens, d_final)
+    keep = (x, d_raw, B, C, dy, init_state, cu_seqlens, d_final)
     return PreparedBwd(dims, tun, lay, args, keep, g, workspace)
 
 
 def ssd_bwd(x, d_raw, d_init, B, C, y, dy, chunk_size=CHUNK, init_state=None,
             cu_seqlens=None, reverse=False, d_final=None, workspace=None, tuning=None,
             grads=None) -> dict:
-    """Gradients of the SSD scan on the GPU: given the forward inputs, the
-    forward output ``y`` and dL/dy (``dy``, same layout rules as y) and
+    """Gradients of the SSD scan on the GPU: given the forward inputs (``y``,
+    the forward output, is accepted for the call's shape but not read; None
+    is fine), dL/dy (``dy``, same layout rules as y) and
     optionally dL/d final_state (``d_final``), returns a dict with dx,
     dd_raw, dB, dC (input dtype, each laid out like its input), dinit_state
     [S,H,N,P] and dd_init [1] (fp32).  Launches on torch's current stream."""

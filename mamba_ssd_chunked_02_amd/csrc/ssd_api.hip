@@ -221,19 +221,21 @@ ssd_layout resolve_layout(const ssd_dims& d, const ssd_layout* lay) {
 }
 
 // Stride rules: >= 0 and <= 2^24 elements; the 16-byte-row tensors' strides
-// a multiple of 16 bytes.  bwd also checks dy's.
+// a multiple of 16 bytes.  The forward checks y's strides, the backward
+// dy's (it does not read y).
 int check_layout(const ssd_dims& d, const ssd_layout& l, bool bwd) {
     const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
     const int64_t per_unit = 16 / esz;
     const int64_t lim = (int64_t)1 << 24;
-    const int64_t all[] = {l.x_token, l.x_head, l.d_raw_token, l.d_raw_head, l.B_token, l.B_group,
-                           l.C_token, l.C_group, l.y_token, l.y_head, l.dy_token, l.dy_head};
-    for (int i = 0; i < (bwd ? 12 : 10); ++i)
-        if (all[i] < 0 || all[i] > lim) return SSD_ERR_SHAPE;
+    const int64_t out_t = bwd ? l.dy_token : l.y_token, out_h = bwd ? l.dy_head : l.y_head;
+    const int64_t all[] = {l.x_token, l.x_head, l.d_raw_token, l.d_raw_head, l.B_token,
+                           l.B_group, l.C_token, l.C_group, out_t, out_h};
+    for (int64_t v : all)
+        if (v < 0 || v > lim) return SSD_ERR_SHAPE;
     const int64_t rows[] = {l.x_token, l.x_head, l.B_token, l.B_group, l.C_token, l.C_group,
-                            l.y_token, l.y_head, l.dy_token, l.dy_head};
-    for (int i = 0; i < (bwd ? 10 : 8); ++i)
-        if (rows[i] % per_unit) return SSD_ERR_ALIGN;
+                            out_t, out_h};
+    for (int64_t v : rows)
+        if (v % per_unit) return SSD_ERR_ALIGN;
     return SSD_OK;
 }
 
@@ -592,12 +594,13 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
                const void* y, const void* dy, const float* d_final, void* dx, void* dd_raw,
                void* dB, void* dC, float* dinit_state, float* dd_init, void* workspace,
                size_t workspace_bytes, void* stream) {
+    (void)y;  // not read: every gradient is formed from the inputs and the states
     BPlan bp;
     const int st = make_bwd_plan(dims, tuning, &bp);
     if (st != SSD_OK) return st;
     const ssd_dims& d = *dims;
     const int64_t T = (int64_t)d.batch * d.seqlen;
-    if (T > 0 && (!x || !d_raw || !B || !C || !y || !dy || !dx || !dd_raw || !dB || !dC))
+    if (T > 0 && (!x || !d_raw || !B || !C || !dy || !dx || !dd_raw || !dB || !dC))
         return SSD_ERR_NULL_ARG;
     if (d.nseq > 0 && !cu_seqlens) return SSD_ERR_NULL_ARG;
     if (d.nseq == 0 && cu_seqlens) return SSD_ERR_SHAPE;
@@ -606,8 +609,8 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
     const int lc = check_layout(d, lay, true);
     if (lc != SSD_OK) return lc;
     const int64_t esz = d.dtype == SSD_BF16 ? 2 : 4;
-    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(dy) ||
-        !aligned16(dx) || !aligned16(dB) || !aligned16(dC))
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dB) || !aligned16(dC))
         return SSD_ERR_ALIGN;
     if (((uintptr_t)d_raw % esz) || ((uintptr_t)dd_raw % esz)) return SSD_ERR_ALIGN;
     if (((uintptr_t)init_state & 3u) || ((uintptr_t)d_final & 3u) || ((uintptr_t)dinit_state & 3u) ||
@@ -728,7 +731,6 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
     q.d_raw = d_raw;
     q.B = B;
     q.C = C;
-    q.y = y;
     q.dy = dy;
     q.hprev = ws + bp.off_sa;
     q.gout = ws + bp.off_sb;
@@ -743,8 +745,6 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
     q.ntok = T;
     q.xs_t = lay.x_token;
     q.xs_h = lay.x_head;
-    q.ys_t = lay.y_token;
-    q.ys_h = lay.y_head;
     q.gs_t = lay.dy_token;
     q.gs_h = lay.dy_head;
     q.ds_t = lay.d_raw_token;

@@ -14,12 +14,23 @@
 //   dB_s = d_s [ sum_{t>=s} (dy_t.X_s) L[t][s] C_t + e^{cs_last-cs_s} Gout X_s ]
 //   dC_t = sum_{s<=t} (dy_t.X_s) L[t][s] d_s B_s + e^{cs_t} Hprev dy_t
 //   dw_s = (dX_s / d_s) . X_s                     (gradient of the input weight)
-//   da_t = <Gout, Hend> + sum_{j>=t} (dy_j.y_j - d_j dw_j)   (log-decay gradient)
-//   <Gout, Hend> = e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last-cs_s} d_s (B_s Gout).X_s
+//   da_t = e^{-d_t} <G_t, H_{t-1}>                (gradient of the log-decay)
 //   d d_raw_t = (dw_t - da_t) sigmoid(d_raw_t + d_init)
 //
-// The da identity follows from <G_t, H_t> = dy_t.y_t + <G_{t+1}, e^{-d_{t+1}} H_t>
-// and keeps every sum inside one chunk.  dB and dC are summed over the heads
+// With G_t = e^{cs_last-cs_t} Gout + sum_{j>=t} e^{cs_j-cs_t} C_j^T dy_j and
+// e^{-d_t} H_{t-1} = e^{cs_t} Hprev + sum_{s<t} e^{cs_t-cs_s} d_s B_s^T X_s,
+// da_t is written out term by term, every term decayed and formed from the
+// inputs in fp32:
+//   da_t = e^{cs_last} <Gout, Hprev>                          (T1)
+//        + sum_{s<t} e^{cs_last-cs_s} d_s (B_s Gout).X_s      (T2, prefix)
+//        + sum_{j>=t} e^{cs_j} (C_j Hprev).dy_j               (T3, suffix)
+//        + sum_{j>=t} sum_{s<t} M[j][s]                       (T4, rectangle)
+// with M[j][s] = L[j][s] d_s (C_j.B_s)(dy_j.X_s).  T4 telescopes over the
+// strict row and column sums of M: T4_t = sum_{k<t} (col_k - row_k), col_k =
+// sum_{j>k} M[j][k], row_k = sum_{s<k} M[k][s].  (The shorter identity da_t =
+// <Gout, Hend> + sum_{j>=t} (dy_j.y_j - d_j dw_j) reaches the same value
+// through sums that cancel: at strong decay they lose the result to the
+// rounding of y.)  dB and dC are summed over the heads
 // of a group: a workgroup takes a subset of those heads and accumulates in
 // registers; the subsets' fp32 partials are added by bwd_reduce.
 #include "ssd_device.h"
@@ -106,7 +117,6 @@ struct __attribute__((aligned(16))) BSmem {
     T cs[kChunk * N];          // C
     T xs[kChunk * kPGroup];    // X of the head (blocks past the headdim stay 0)
     T gy[kChunk * kPGroup];    // dL/dy
-    T ys[kChunk * kPGroup];    // y
     T gr[kPGroup * N];         // Gout (entries past P*N stay 0)
     T hr[kPGroup * N];         // Hprev
     f32x4 cb[kTiles][64];      // C B^T blocks (t rows, s columns), result order
@@ -115,7 +125,10 @@ struct __attribute__((aligned(16))) BSmem {
     X4 f3[kTiles][64];         // the same product transposed (rows s): dC
     BDecay dec[3];                 // factors of the last, this and the next head
     __attribute__((aligned(16))) uint32_t dr[kBwdMaxHeads][kChunk];  // d_raw of every head of the workgroup
-    float red[3][kWaves][kChunk];  // per-wave partial dw, zx, dy.y
+    float red[2][kWaves][kChunk];  // per-wave partial dw, zx
+    float t3[2][kChunk];           // per-quad partial (C_t Hprev).dy_t e^{cs_t}
+    float rp[2][kTiles][16];       // strict row sums of M per block (two heads' worth)
+    float cp[2][kTiles][16];       // strict column sums of M per block
     float gh[8];                   // per-wave partial <Gout, Hprev>
 };
 
@@ -172,28 +185,39 @@ __device__ __forceinline__ f32x8 state_frag_t(const float* st, int nb, int kp, i
 }
 
 // Masked block (TB, SB) in (t rows, s columns) orientation: lane (s, g) holds
-// t = 16TB + 4g + i.  ws = d_s or 1.
-template <typename T>
-__device__ __forceinline__ typename Vec<T>::x4 mask_ts(const f32x4& acc, const BDecay& D, int TB,
-                                                      int SB, int lane, int clen, bool with_d) {
-    typename Vec<T>::x4 v;
+// t = 16TB + 4g + i, times d_s when with_d; in fp32, and rounded to T.
+__device__ __forceinline__ f32x4 mask_ts_f(const f32x4& acc, const BDecay& D, int TB, int SB,
+                                           int lane, int clen, bool with_d) {
+    f32x4 v;
     const int s = 16 * SB + (lane & 15), t0 = 16 * TB + 4 * (lane >> 4);
     const float ds = with_d ? D.dt[s] : 1.f;
     if (TB > SB) {
         const float f = D.fm[TB * (TB - 1) / 2 + SB] * D.fa0[s] * ds;
         const f32x4 fb = *(const f32x4*)&D.fb[t0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = cvt<T>(acc[i] * (fb[i] * f));
+        for (int i = 0; i < 4; ++i) v[i] = acc[i] * (fb[i] * f);
     } else {
         const float css = D.cs2[s];
         const f32x4 cst = *(const f32x4*)&D.cs2[t0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool ok = s <= t0 + i && t0 + i < clen;
-            v[i] = cvt<T>(ok ? acc[i] * fexp2(cst[i] - css) * ds : 0.f);
+            v[i] = ok ? acc[i] * fexp2(cst[i] - css) * ds : 0.f;
         }
     }
     return v;
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x4 round4(const f32x4& a) {
+    typename Vec<T>::x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = cvt<T>(a[i]);
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x4 mask_ts(const f32x4& acc, const BDecay& D, int TB,
+                                                      int SB, int lane, int clen, bool with_d) {
+    return round4<T>(mask_ts_f(acc, D, TB, SB, lane, clen, with_d));
 }
 // Masked block (TB, SB) in (s rows, t columns) orientation: lane (t, g) holds
 // s = 16SB + 4g + i, times d_s.
@@ -327,7 +351,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     float ddi = 0.f;
     const X4 z4 = {};
 
-    // A head's X, dy and y tiles, its two states and its d_raw go through
+    // A head's X and dy tiles, its two states and its d_raw go through
     // registers: the next head's loads are issued as soon as this head's
     // data is in LDS, and written to LDS after this head's last LDS read, so
     // their latency hides behind this head's products.  Tile rows follow the
@@ -336,7 +360,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     constexpr int TI = (4 * W + kBWaves - 1) / kBWaves;  // tile units per lane
     constexpr int SI = (kPGroup * N * (int)sizeof(T) / 1024 + kBWaves - 1) / kBWaves;  // state units
-    u32x4 rx[TI], ry[TI], ryy[TI], rg[SI], rh[SI];
+    u32x4 rx[TI], ry[TI], rg[SI], rh[SI];
     auto tile_off = [&](int i, int64_t rstride) -> int64_t {
         const int j = (i % W) * 64 + lane;
         const int pr = j / W, pu = j % W;
@@ -350,14 +374,12 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         const int npb = ucols(u) / 16, PN = ucols(u) * N;
         const T* xr = (const T*)p.x + tb0 * p.xs_t + h * p.xs_h + pcol0;
         const T* gr = (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h + pcol0;
-        const T* yr = (const T*)p.y + tb0 * p.ys_t + h * p.ys_h + pcol0;
 #pragma unroll
         for (int k = 0; k < TI; ++k) {
             const int i = wave + kBWaves * k;
             if (i < 4 * W && i / W < npb) {
                 rx[k] = *(const u32x4*)(xr + tile_off(i, dir * p.xs_t));
                 ry[k] = *(const u32x4*)(gr + tile_off(i, dir * p.gs_t));
-                ryy[k] = *(const u32x4*)(yr + tile_off(i, dir * p.ys_t));
             }
         }
         const int64_t hb = (chunk * p.H + h) * (int64_t)P * N + (int64_t)pcol0 * N;
@@ -390,7 +412,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 const bool in = i / W < npb;
                 *(u32x4*)(sm.xs + o) = in ? rx[k] : z;
                 *(u32x4*)(sm.gy + o) = in ? ry[k] : z;
-                *(u32x4*)(sm.ys + o) = in ? ryy[k] : z;
             }
         }
 #pragma unroll
@@ -421,29 +442,40 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         dd_at = -1;
     };
 
-    // per-token sums of unit u -> its part of d d_raw (wave 0, lane = token)
+    // per-token sums of unit u -> its part of d d_raw (wave 0, lane = token):
+    // da from its four terms (T1 + T2 + T3 + T4 above)
     auto tail = [&](int u) {
         const int h = h0 + u / npg;
         const BDecay& D = sm.dec[u % 3];
+        const int par = u & 1;
         store_dd();
-        const int s = lane;
-        float dw = 0.f, zx = 0.f, yy = 0.f, ghs = 0.f;
+        const int s = lane, sbk = s >> 4, sl = s & 15;
+        float dw = 0.f, zx = 0.f, ghs = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             dw += sm.red[0][w][s];
             zx += sm.red[1][w][s];
-            yy += sm.red[2][w][s];
         }
 #pragma unroll
         for (int w = 0; w < kBWaves; ++w) ghs += sm.gh[w];
+        // strict row sum (blocks (sbk, b), b <= sbk) and column sum (blocks
+        // (b, sbk), b >= sbk) of M at token s
+        float row = 0.f, col = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b <= sbk) row += sm.rp[par][tix(sbk, b)][sl];
+            if (b >= sbk) col += sm.cp[par][tix(b, sbk)][sl];
+        }
         const bool in = s < clen;
         const float ds = D.dt[s];
-        // <Gout, Hend>: e^{cs_last} <Gout, Hprev> + sum_s e^{cs_last - cs_s} d_s zx_s
-        const float ez = lane_value(wave_prefix_sum(in ? D.wl[s] * ds * zx : 0.f), 63);
-        const float E = D.fe[kChunk - 1] * ghs + ez;
-        const float r = in ? yy - ds * dw : 0.f;
-        const float incl = wave_prefix_sum(r);
-        const float da = E + lane_value(incl, 63) - incl + r;  // E + sum_{j >= s} r_j
+        const float v2 = in ? D.wl[s] * ds * zx : 0.f;
+        const float v3 = in ? sm.t3[0][s] + sm.t3[1][s] : 0.f;
+        const float v4 = in ? col - row : 0.f;
+        const float p2 = wave_prefix_sum(v2) - v2;                // T2: s' < s
+        const float p3 = wave_prefix_sum(v3);
+        const float s3 = lane_value(p3, 63) - p3 + v3;            // T3: j >= s
+        const float p4 = wave_prefix_sum(v4) - v4;                // T4: k < s
+        const float da = D.fe[kChunk - 1] * ghs + p2 + s3 + p4;
         const float gr = (dw - da) * D.sg[s];
         dd_acc = u % npg == 0 ? gr : dd_acc + gr;
         if (u % npg == npg - 1) {
@@ -464,7 +496,10 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
 
         // masked blocks, 30 units (block ti, kind): A1 = (C B^T) o L; A2 =
         // (dy X^T) o L d_s in both orientations; wave w takes units w - 1,
-        // w + 7, ... (the first and the last wave three, the others four)
+        // w + 7, ... (the first and the last wave three, the others four).
+        // The block sums of M go to the slots of this head's parity: the
+        // tail of the previous head may still read the other ones.
+        const int upar = u & 1;
         for (int u = (wave + kBWaves - 1) % kBWaves; u < 3 * kTiles; u += kBWaves) {
             const int kind = u / kTiles, ti = u % kTiles;
             int TB, SB;
@@ -479,8 +514,32 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                     const X8 xs = tile_frag<kPGroup>(sm.xs, 16 * SB + l16, kp, g);
                     m = kind == 1 ? mma(yt, xs, m) : mma(xs, yt, m);
                 }
-                if (kind == 1) sm.f2[ti][lane] = mask_ts<T>(m, D, TB, SB, lane, clen, true);
-                else sm.f3[ti][lane] = mask_st<T>(m, D, TB, SB, lane, clen);
+                if (kind == 1) {
+                    const f32x4 mf = mask_ts_f(m, D, TB, SB, lane, clen, true);
+                    sm.f2[ti][lane] = round4<T>(mf);
+                    // M = (C B^T) o L d_s o (dy X^T) off the diagonal (s < t),
+                    // in fp32; its row sums over the block's 16 columns s
+                    // (lane 15 of each row ends with the sum) and column sums
+                    // over its 16 rows t, for T4
+                    const f32x4 cbv = sm.cb[ti][lane];
+                    const int sc = 16 * SB + l16, t0 = 16 * TB + 4 * g;
+                    f32x4 mm;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mm[i] = (TB > SB || sc < t0 + i) ? mf[i] * cbv[i] : 0.f;
+                    float cs = (mm[0] + mm[1]) + (mm[2] + mm[3]);
+                    cs = xor_add(xor_add(cs, 16), 32);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        mm[i] = dpp_add<0x111, 0xf>(mm[i]);  // row_shr:1
+                        mm[i] = dpp_add<0x112, 0xf>(mm[i]);  // row_shr:2
+                        mm[i] = dpp_add<0x114, 0xf>(mm[i]);  // row_shr:4
+                        mm[i] = dpp_add<0x118, 0xf>(mm[i]);  // row_shr:8
+                    }
+                    if (g == 0) sm.cp[upar][ti][l16] = cs;
+                    if (l16 == 15) *(f32x4*)&sm.rp[upar][ti][4 * g] = mm;
+                } else {
+                    sm.f3[ti][lane] = mask_st<T>(m, D, TB, SB, lane, clen);
+                }
             }
         }
         if (wave == kFW && u + 1 < nunit)
@@ -520,22 +579,17 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 if (s < clen)
                     store4_async((T*)p.dx + tok(s) * p.xs_t + h * p.xs_h + pcol0 + 16 * w4 + 4 * g, ds * raw);
                 const X4 xv = tld4(sm.xs, s, w4, 4 * g);
-                const X4 gv = tld4(sm.gy, s, w4, 4 * g);
-                const X4 yv = tld4(sm.ys, s, w4, 4 * g);
-                float dw = 0.f, zx = 0.f, yy = 0.f;
+                float dw = 0.f, zx = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     dw += raw[i] * (float)xv[i];
                     zx += accG[i] * (float)xv[i];
-                    yy += (float)gv[i] * (float)yv[i];
                 }
                 dw = xor_add(xor_add(dw, 16), 32);
                 zx = xor_add(xor_add(zx, 16), 32);
-                yy = xor_add(xor_add(yy, 16), 32);
                 if (g == 0) {
                     sm.red[0][w4][s] = dw;
                     sm.red[1][w4][s] = zx;
-                    sm.red[2][w4][s] = yy;
                 }
             }
 #pragma unroll
@@ -549,7 +603,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 3; ++k)
+            for (int k = 0; k < 2; ++k)
                 if (lane < 32) sm.red[k][w4][32 * q + lane] = 0.f;
         }
         gh = wave_prefix_sum(gh);
@@ -583,7 +637,9 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                     dBt[i] = mma(state_frag_t<NB>(sm.gr, nb, kp, g, lane), xw[kp], dBt[i]);
             }
         }
-        // dC for tokens t in block w4: sum_s A2[t][s] d_s B_s + e^{cs_t} Hprev dy_t
+        // dC for tokens t in block w4: sum_s A2[t][s] d_s B_s + e^{cs_t} Hprev dy_t;
+        // the head's own e^{cs_t} Hprev dy_t (rows n = 16nb + 4g + k) dotted
+        // with C_t gives its part of T3
         {
             const int TB = w4;
             X8 a3[2];
@@ -598,6 +654,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
             X8 gw[2];
 #pragma unroll
             for (int kp = 0; kp < 2; ++kp) gw[kp] = scale8<T>(tile_frag<kPGroup>(sm.gy, t, kp, g), fe);
+            float t3 = 0.f;
 #pragma unroll
             for (int i = 0; i < NBH; ++i) {
                 const int nb = q * NBH + i;
@@ -606,10 +663,18 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 for (int j = 0; j < 2; ++j)
                     if (2 * j <= TB)
                         dCt[i] = mma(tok_frag(sm.bs, 32 * j + 4 * g, 32 * j + 16 + 4 * g, nb, lane), a3[j], dCt[i]);
+                f32x4 hd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kp = 0; kp < 2; ++kp)
-                    dCt[i] = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], dCt[i]);
+                for (int kp = 0; kp < 2; ++kp) hd = mma(state_frag_t<NB>(sm.hr, nb, kp, g, lane), gw[kp], hd);
+                const X4 cv = tld4(sm.cs, t, nb, 4 * g);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    dCt[i][k] += hd[k];
+                    t3 += hd[k] * (float)cv[k];
+                }
             }
+            t3 = xor_add(xor_add(t3, 16), 32);
+            if (g == 0) sm.t3[q][t] = t3;
         }
         block_sync();  // every read of this head's tiles and states is done
     }

@@ -78,7 +78,6 @@ struct BParams {
     const void* d_raw;      // [b, L, H]
     const void* B;          // [b, L, G, N]
     const void* C;
-    const void* y;          // forward output (strides ys_t, ys_h)
     const void* dy;         // dL/dy (strides gs_t, gs_h)
     const void* hprev;      // [nchunk][H][P*N] state entering each chunk
     const void* gout;       // [nchunk][H][P*N] dL/d(state leaving each chunk)
@@ -90,7 +89,7 @@ struct BParams {
     const int32_t* cu;      // sanitized cu_seqlens (varlen) or null
     const int4* table;      // [nchunk] {seq, chunk, 1, 0} (varlen)
     int64_t L, ntok;        // tokens per batch row, b * L
-    int64_t xs_t, xs_h, ys_t, ys_h, gs_t, gs_h;
+    int64_t xs_t, xs_h, gs_t, gs_h;
     int64_t ds_t, ds_h;     // d_raw (and dd_raw) strides: token, head
     int64_t bs_t, bs_g;     // B (and dB) strides: token, group
     int64_t cs_t, cs_g;     // C (and dC) strides: token, group

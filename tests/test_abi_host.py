@@ -358,7 +358,11 @@ def test_bwd_rejects_bad_arguments(m):
     assert call_bwd(m, None) == -1
     assert call_bwd(m, ok, dy=None) == -1                                  # NULL_ARG
     assert call_bwd(m, ok, dB=None) == -1
-    assert call_bwd(m, ok, y=None) == -1
+    # y is not read: NULL, a misaligned pointer or bad y strides pass the
+    # argument checks (the NULL workspace then stops the call)
+    assert call_bwd(m, ok, y=None, ws=None) == -6
+    assert call_bwd(m, ok, y=FAKE + 4, ws=None) == -6
+    assert call_bwd(m, ok, layout=lay(m, ok, y_token=1 << 25), ws=None) == -6
     assert call_bwd(m, m.make_dims(1, 128, 2, 64, 256)) == -5
     assert call_bwd(m, m.make_dims(1, 128, 2, 24, 128)) == -2
     assert call_bwd(m, m.make_dims(1, 128, 2, 64, 128, nseq=2)) == -1      # cu_seqlens missing

@@ -4,9 +4,9 @@ pinned by finite differences in test_oracle_bwd_pins.py).
 
 Bound per gradient (max|gpu - ref| / max|ref|): BWD_TOL for bf16 inputs
 (fp32 accumulation; the operands of every product are rounded to bf16,
-states included), 1e-5 for fp32 inputs.  The forward output y the backward
-reads is the GPU's own, as a caller would pass it; dy and d_final are seeded
-Gaussians.
+states included), 1e-5 for fp32 inputs.  The library does not read the
+forward output y; the tests pass the GPU's own, as a caller would, or None.
+dy and d_final are seeded Gaussians.
 """
 import numpy as np
 import pytest
@@ -293,8 +293,7 @@ def test_bwd_projection_views(ssd, reverse):
     buffer; the gradients go straight into the same places of a gradient
     buffer of that layout (each gradient is written with its input's
     strides); against the adjoint oracle on contiguous copies."""
-    # H = 8 keeps a projection row a whole number of 16-byte units; d_init
-    # is the workloads' (strong decay is test_bwd_dd_raw_strong_decay's case)
+    # H = 8 keeps a projection row a whole number of 16-byte units
     p = random_problem(361, 2, 300, 8, 64, 64, ngroups=2, dtype="bf16", init_scale=0.5,
                        d_init=-4.6)
     b, L, H, P = p["x"].shape
@@ -348,29 +347,31 @@ def test_bwd_projection_views(ssd, reverse):
         assert v <= BWD_TOL[torch.bfloat16], (k, v)
 
 
-@pytest.mark.xfail(strict=True, reason=(
-    "d d_raw precision at strong decay: the gradient kernel forms the log-decay "
-    "gradient from a chunk-local identity whose per-token terms (dy.y - d dw) are "
-    "much larger than the result, so their bf16 rounding adds up over the chunk "
-    "(1.28e-2 measured on this problem, reverse direction)"))
-def test_bwd_dd_raw_strong_decay(ssd):
-    """Step sizes around 0.2 (d_init -2): the d d_raw bound on the problem
-    whose reverse direction first showed the precision limit."""
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_dd_raw_strong_decay(ssd, reverse):
+    """Step sizes around 0.2 (d_init -2), the problem whose reverse direction
+    showed the precision limit of the chunk-local identity for the log-decay
+    gradient (1.28e-2 on d d_raw); the kernel's term-by-term form meets the
+    bf16 bound.  y is passed as None: the library does not read it."""
     p = random_problem(361, 2, 300, 8, 64, 64, ngroups=2, dtype="bf16", init_scale=0.5,
                        d_init=-2.0)
     d = {k: (_dev(v) if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
     b, L, H, P = p["x"].shape
     N = p["B"].shape[3]
-    y, _ = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
-                       init_state=d["init_state"], reverse=True)
     g = torch.Generator().manual_seed(13)
     dy = torch.randn((b, L, H, P), generator=g).to(torch.bfloat16)
     dfin = torch.randn((b, H, N, P), generator=g)
-    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y, _dev(dy),
-                      init_state=d["init_state"], reverse=True, d_final=_dev(dfin))
+    got = ssd.ssd_bwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], None, _dev(dy),
+                      init_state=d["init_state"], reverse=reverse, d_final=_dev(dfin))
     torch.cuda.synchronize()
     ref = O.ssd_ref_bwd(p["x"], p["d_raw"], p["d_init"], p["B"], p["C"], dy,
-                        init_state=p["init_state"], d_final=dfin, reverse=True)
-    err = F.rel_err(got["dd_raw"].float().cpu(), ref["dd_raw"])
-    print(f"bwd strong decay rev dd_raw={err:.2e}", flush=True)
-    assert err <= BWD_TOL[torch.bfloat16]
+                        init_state=p["init_state"], d_final=dfin, reverse=reverse)
+    errs = {k: F.rel_err(got[k].float().cpu(), ref[k]) for k in KEYS}
+    errs["dd_init"] = dd_init_err(float(got["dd_init"].cpu()), ref)
+    print(f"bwd strong decay rev={reverse} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+    for k, v in errs.items():
+        assert v <= BWD_TOL[torch.bfloat16], (k, v)
+    # d d_raw at the level of the other gradients (3.0e-3 measured), well
+    # inside the bound that the cancelling identity exceeded
+    assert errs["dd_raw"] <= 5e-3
