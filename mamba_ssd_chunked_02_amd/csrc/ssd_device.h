@@ -120,6 +120,20 @@ __device__ __forceinline__ float lane_value(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Read one word of every 64-byte line of a kernel's argument block at entry,
+// all in one batch.  The compiler otherwise loads the fields it needs in
+// several dependent groups as the code reaches them, and each group waits a
+// memory round trip for lines no cache holds yet; after this, those loads hit
+// the scalar cache.
+template <typename P>
+__device__ __forceinline__ void touch_args(const P& p) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&p);
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(P) / 4); i += 16) x ^= w[i];
+    asm volatile("" ::"s"(x));
+}
+
 // Raw v_exp_f32: every argument here is <= 0, results below 2^-126 flush to 0.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

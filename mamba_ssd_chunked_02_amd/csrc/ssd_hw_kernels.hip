@@ -234,6 +234,7 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE
     constexpr int NB = Cf::NB, KN = Cf::KN, WPH = Cf::WPH, NW = Cf::NW;
     constexpr bool SCAN = MODE == kHwScan;
     __shared__ Sm sm;
+    touch_args(p);
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
     // head groups, which share B and C) land on the same XCD and its L2.

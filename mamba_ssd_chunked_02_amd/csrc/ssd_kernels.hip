@@ -259,8 +259,20 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     // decode divides in 32 bits)
     const uint32_t lg32 = (uint32_t)logical, rest = lg32 / (uint32_t)p.npg;
     const int pg = (int)(lg32 - rest * (uint32_t)p.npg);
-    const uint32_t span32 = rest / (uint32_t)ngrp;
+    uint32_t span32 = rest / (uint32_t)ngrp;
     const int hgi = (int)(rest - span32 * (uint32_t)ngrp);
+    if (MODE != kModeFused && !p.nseq && p.batch > 1) {
+        // Interleave the sequences' spans, each odd sequence's in reverse
+        // order: neighbouring logical spans (one XCD) then pair early and
+        // late positions, so the XCDs share the fold's re-reads of earlier
+        // span states evenly instead of one XCD holding every late span.
+        // Within a pair the later position (the longer fold) comes first:
+        // an XCD's first workgroups each get a CU of their own.
+        const uint32_t B = (uint32_t)p.batch, S = (uint32_t)p.sps;
+        const uint32_t k = span32 / B, j = span32 % B;
+        const uint32_t sq = 2u * k < S ? B - 1u - j : j;
+        span32 = sq * S + ((sq & 1u) ? S - 1u - k : k);
+    }
     const int64_t span = span32;
     const int h0 = hgi * hg;
     const int nh = min(hg, p.H - h0);  // hg <= HG divides H/G: one B/C group
@@ -732,6 +744,7 @@ template <typename T, int N, int HG, int MODE>
 __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) void span_kernel(
     KParams p) {
     __shared__ Smem<T, N, HG, !is_state(MODE)> sm;
+    touch_args(p);
     span_body<T, N, HG, MODE>(p, blockIdx.x, sm);
 }
 
@@ -743,8 +756,13 @@ template <typename T, int N>
 __global__ __launch_bounds__(kThreads, (span_occupancy<T, N, 1, kModeState>())) void span_state_pair_kernel(
     KParams pa, KParams pb, int64_t na) {
     __shared__ Smem<T, N, 1, false> sm;
-    if ((int64_t)blockIdx.x < na) span_body<T, N, 1, kModeState>(pa, blockIdx.x, sm);
-    else span_body<T, N, 1, kModeStateGrad>(pb, blockIdx.x - na, sm);
+    if ((int64_t)blockIdx.x < na) {
+        touch_args(pa);
+        span_body<T, N, 1, kModeState>(pa, blockIdx.x, sm);
+    } else {
+        touch_args(pb);
+        span_body<T, N, 1, kModeStateGrad>(pb, blockIdx.x - na, sm);
+    }
 }
 
 // A 16-byte store the compiler's wait counting does not see (the s_nop
@@ -854,6 +872,7 @@ __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
 
 template <typename TS>
 __global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
+    touch_args(p);
     state_pass_body<TS>(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
@@ -861,8 +880,13 @@ __global__ __launch_bounds__(256) void state_pass_kernel(KParams p) {
 // spans, the rest pb's.
 template <typename TS>
 __global__ __launch_bounds__(256) void state_pass_pair_kernel(KParams pa, KParams pb, int64_t na) {
-    if ((int64_t)blockIdx.x < na) state_pass_body<TS>(pa, (int64_t)blockIdx.x * 256 + threadIdx.x);
-    else state_pass_body<TS>(pb, ((int64_t)blockIdx.x - na) * 256 + threadIdx.x);
+    if ((int64_t)blockIdx.x < na) {
+        touch_args(pa);
+        state_pass_body<TS>(pa, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    } else {
+        touch_args(pb);
+        state_pass_body<TS>(pb, ((int64_t)blockIdx.x - na) * 256 + threadIdx.x);
+    }
 }
 
 // Zero words [0, nwords) of the workspace header and the fused launch's
