@@ -269,7 +269,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     constexpr int NB = Cf::NB, KN = Cf::KN, W = Cf::W, BI = Cf::BI, EPU = Cf::EPU;
     constexpr int NBH = (NB + 1) / 2;  // state-row blocks per quad
     __shared__ BSmem<T, N> sm;
-    touch_args(p);
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int l16 = lane & 15, g = lane >> 4;
     const int q = wave >> 2, w4 = wave & 3;
