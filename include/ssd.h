@@ -236,7 +236,18 @@ enum {
  * the stages in stage_mask, for callers that time or interleave work
  * between stages.  Running the stages in the order above on one stream with
  * one workspace (left untouched in between) and the same tuning gives
- * exactly ssd_fwd_ex's result with SSD_STAGE_ALL. */
+ * exactly ssd_fwd_ex's result with SSD_STAGE_ALL.
+ *
+ * Between stages the workspace can be read (span kernels, fused_pass 0 or
+ * 1; for inspection and tests).  After SSD_STAGE_STATE, bytes from 256 hold
+ * nspan x H span states of P x N entries, state_bytes each (span s = sequence
+ * x spans per sequence + span within it; spans run from the end of a sequence
+ * when reverse is set): the state of the span's tokens from a zero state,
+ * entry (n, p) at ((p / 16 * N/16 + n / 16) * 64 + lane) * 4 + i with lane =
+ * 16 (n % 16 / 4) + p % 16, i = n % 4.  The nspan x H float32 decay products
+ * exp(-sum of d over the span) follow at the next 256-byte boundary.  After
+ * SSD_STAGE_PASS (fused_pass 0) each state slot holds the state entering its
+ * span instead. */
 int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuning,
                const ssd_layout* layout,
                const void* x, const void* d_raw, float d_init,

@@ -494,3 +494,97 @@ def test_state_f32_option(ssd, cfg):
         assert max(errs[opt]) <= 1e-2
     print(f"{w.name} bf16 states y/final err {errs[0][0]:.3e}/{errs[0][1]:.3e}, "
           f"f32 states {errs[1][0]:.3e}/{errs[1][1]:.3e}", flush=True)
+
+
+# ------------------------------------------------------------ stage level
+def _span_states(ssd, call, plan, H, P, N):
+    """The span states and decays that the state stage (and, in plan 0, the
+    pass) leave in the workspace, as [nspan][H][N][P] float and [nspan][H]:
+    states from byte 256 in MFMA result order (entry (n, p) at
+    ((pb * N/16 + nb) * 64 + lane) * 4 + i, n = 16 nb + 4 (lane / 16) + i,
+    p = 16 pb + lane % 16), the decays at the next 256-byte boundary."""
+    ws = call.workspace
+    ns, esz = plan.nspan, plan.state_bytes
+    n = ns * H * P * N
+    raw = ws[256:256 + n * esz].view(torch.bfloat16 if esz == 2 else torch.float32)
+    a = raw.float().cpu().reshape(ns, H, P // 16, N // 16, 4, 16, 4)
+    st = a.permute(0, 1, 3, 4, 6, 2, 5).reshape(ns, H, N, P)
+    off = (256 + n * esz + 255) // 256 * 256
+    dec = ws[off:off + ns * H * 4].view(torch.float32).cpu().reshape(ns, H)
+    return st.double().numpy(), dec.double().numpy()
+
+
+def _span_ranges(L, K, j, reverse):
+    """Tokens of span j (K chunks of 64) of a length-L sequence, in the
+    original order; with reverse the spans run from the sequence's end."""
+    a, b = 64 * K * j, min(64 * K * (j + 1), L)
+    return (L - b, L - a) if reverse else (a, b)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("dtype,f32_states", [("bf16", 0), ("bf16", 1), ("f32", 0)])
+def test_stage_span_states_and_pass(ssd, dtype, f32_states, reverse):
+    """Stage-level parity of plan 0: after the state stage alone, every
+    span's local state (from a zero state over its own tokens) and its decay
+    product against the oracle run on that span's tokens; after the pass
+    stage, every span slot holds the state entering the span (the oracle's
+    state after the tokens before it, from init_state) and final_state the
+    state after the whole sequence.  Two sequences of 13 chunks (spans of
+    4, 4, 4 and 1 chunks, the last one ragged) and two column groups."""
+    b, L, H, P, N = 2, 64 * 12 + 17, 3, 80, 64
+    p = random_problem(211, b, L, H, P, N, dtype=dtype, init_scale=0.5, d_init=-3.0)
+    d = to_dev(p)
+    tun = {"kernel": "span", "state_pass": "pass", "chunks_per_span": 4, "state_f32": f32_states}
+    call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"],
+                       reverse=reverse, tuning=tun)
+    plan = ssd.ssd_fwd_plan(call.dims, tun)
+    assert plan.fused_pass == 0 and plan.head_wave == 0 and plan.chunks_per_span == 4
+    sps = plan.nspan // b
+    assert sps == 4
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    dd = O.delta(O.as_f64(p["d_raw"]), p["d_init"])
+
+    call.run(ssd.STAGE_TABLE | ssd.STAGE_STATE)
+    torch.cuda.synchronize()
+    st, dec = _span_states(ssd, call, plan, H, P, N)
+    ref_st, ref_dec = np.zeros_like(st), np.zeros_like(dec)
+    for s in range(b):
+        for j in range(sps):
+            t0, t1 = _span_ranges(L, 4, j, reverse)
+            sl = lambda t: t[s:s + 1, t0:t1]
+            _, f = O.ssd_ref_seq(sl(p["x"]), sl(p["d_raw"]), p["d_init"], sl(p["B"]), sl(p["C"]),
+                                 reverse=reverse)
+            ref_st[s * sps + j] = f[0]
+            ref_dec[s * sps + j] = -dd[s, t0:t1].sum(axis=0)
+    # decays compared as logs: the kernel sums up to 256 fp32 log-steps
+    es = O.rel_err(st, ref_st)
+    ed = float(np.max(np.abs(np.log(dec) - ref_dec) / np.abs(ref_dec)))
+    print(f"stage state {dtype} f32_states={f32_states} rev={reverse}: states {es:.3e} "
+          f"decays {ed:.3e}", flush=True)
+    assert es <= tol and ed <= 1e-4
+
+    call.run(ssd.STAGE_PASS)
+    torch.cuda.synchronize()
+    st, _ = _span_states(ssd, call, plan, H, P, N)
+    fin = call.final_state.cpu().double().numpy()
+    ref_in, ref_fin = np.zeros_like(st), np.zeros_like(fin)
+    for s in range(b):
+        init = O.as_f64(p["init_state"])[s:s + 1]
+        for j in range(sps):
+            t0, t1 = _span_ranges(L, 4, j, reverse)
+            a, e = (t1, L) if reverse else (0, t0)   # the tokens processed before span j
+            if e > a:
+                sl = lambda t: t[s:s + 1, a:e]
+                _, f = O.ssd_ref_seq(sl(p["x"]), sl(p["d_raw"]), p["d_init"], sl(p["B"]),
+                                     sl(p["C"]), init_state=init, reverse=reverse)
+                ref_in[s * sps + j] = f[0]
+            else:
+                ref_in[s * sps + j] = init[0]
+        sl = lambda t: t[s:s + 1]
+        _, f = O.ssd_ref_seq(sl(p["x"]), sl(p["d_raw"]), p["d_init"], sl(p["B"]), sl(p["C"]),
+                             init_state=init, reverse=reverse)
+        ref_fin[s] = f[0]
+    ei, ef = O.rel_err(st, ref_in), O.rel_err(fin, ref_fin)
+    print(f"stage pass {dtype} f32_states={f32_states} rev={reverse}: incoming {ei:.3e} "
+          f"final {ef:.3e}", flush=True)
+    assert ei <= tol and ef <= tol
