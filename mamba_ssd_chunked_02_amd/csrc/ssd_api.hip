@@ -267,6 +267,9 @@ struct BPlan {
     int64_t nspan4 = 0;    // (varlen) four-chunk span slots of the chunk-state pass
     size_t off_cu4 = 0, off_spoff4 = 0, off_table4 = 0;
     size_t off_sa = 0, off_da = 0, off_sb = 0, off_db = 0;
+    // (four-chunk walks) span-level states and decays of both sets
+    int64_t nspan4s = 0;   // four-chunk span slots (batch or varlen)
+    size_t off_ta = 0, off_ea = 0, off_tb = 0, off_eb = 0;
     size_t off_pb = 0, off_pc = 0, off_pi = 0, total = 0;
 };
 
@@ -317,6 +320,22 @@ int make_bwd_plan(const ssd_dims* d, const ssd_tuning* tun, BPlan* bp) {
     off = align_up(off + states);
     bp->off_db = off;
     off = align_up(off + (size_t)bp->nchunk * d->nheads * sizeof(float));
+    if (bp->state_chunks == 4) {
+        // The chunk-state walks carry the state through each four-chunk
+        // span: per chunk the span-local part, per span the whole (passed
+        // across spans), so the pass walks a quarter of the slots.
+        bp->nspan4s = d->nseq > 0 ? bp->nspan4 : (int64_t)d->batch * ceil_div(bp->cps, 4);
+        const size_t st4 = (size_t)bp->nspan4s * d->nheads * d->headdim * d->d_state * esz;
+        const size_t dc4 = (size_t)bp->nspan4s * d->nheads * sizeof(float);
+        bp->off_ta = off;
+        off = align_up(off + st4);
+        bp->off_ea = off;
+        off = align_up(off + dc4);
+        bp->off_tb = off;
+        off = align_up(off + st4);
+        bp->off_eb = off;
+        off = align_up(off + dc4);
+    }
     bp->off_pb = off;
     off = align_up(off + part);
     bp->off_pc = off;
@@ -709,6 +728,9 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
         for (ssd::KParams* k : {&pa4, &pg4}) {
             k->K = 4;
             k->chunk_out = 1;
+            // the state is carried through each span (the gradient set
+            // walks it backwards); chunk slots keep the span-local parts
+            k->chunk_run = 1;
             if (d.nseq > 0) {
                 k->nspan = bp.nspan4;
                 k->cu = (const int32_t*)(ws + bp.off_cu4);
@@ -720,9 +742,26 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
                 k->nspan = (int64_t)d.batch * k->sps;
             }
         }
+        pg4.walk_rev = 1;
+        pa4.span_states = ws + bp.off_ta;
+        pa4.span_decay = (float*)(ws + bp.off_ea);
+        pg4.span_states = ws + bp.off_tb;
+        pg4.span_decay = (float*)(ws + bp.off_eb);
+    }
+    // the pass: over the chunks, or (four-chunk walks) over the spans'
+    // whole states, leaving in each span slot the state entering the span
+    // (the gradient of the state leaving it, walking backwards)
+    ssd::KParams pas = pa, pgs = pg;
+    if (bp.state_chunks == 4) {
+        pas = pa4;
+        pgs = pg4;
+        pas.states = pa4.span_states;
+        pas.decay = pa4.span_decay;
+        pgs.states = pg4.span_states;
+        pgs.decay = pg4.span_decay;
     }
     e = ssd::launch_span_state_pair(pa4, pg4, d.dtype, d.d_state, s);
-    if (e == hipSuccess) e = ssd::launch_state_pass_pair(pa, pg, d.dtype, s);
+    if (e == hipSuccess) e = ssd::launch_state_pass_pair(pas, pgs, d.dtype, s);
     if (e != hipSuccess) return SSD_ERR_HIP;
 
     ssd::BParams q;
@@ -734,6 +773,14 @@ int ssd_bwd_ex(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout*
     q.dy = dy;
     q.hprev = ws + bp.off_sa;
     q.gout = ws + bp.off_sb;
+    if (bp.state_chunks == 4) {
+        q.hspan = ws + bp.off_ta;
+        q.gspan = ws + bp.off_tb;
+        q.hdec = (const float*)(ws + bp.off_da);
+        q.gdec = (const float*)(ws + bp.off_db);
+        q.span_off4 = d.nseq > 0 ? (const int32_t*)(ws + bp.off_spoff4) : nullptr;
+        q.sps4 = (int32_t)ceil_div(bp.cps, 4);
+    }
     q.dx = dx;
     q.dd_raw = dd_raw;
     q.dB_part = (float*)(ws + bp.off_pb);

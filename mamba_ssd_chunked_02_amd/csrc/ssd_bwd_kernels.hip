@@ -273,7 +273,16 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     const int l16 = lane & 15, g = lane >> 4;
     const int q = wave >> 2, w4 = wave & 3;
 
-    const int64_t item = blockIdx.x;
+    // XCD-aware order: workgroups are dealt to the XCDs round-robin, and each
+    // XCD takes a contiguous run of work items (the remainder spread over the
+    // first XCDs), so the head subsets of a chunk (which share its B and C
+    // tiles) and the chunks of a span (which share its entering states) meet
+    // in one L2.
+    const int64_t item = [] {
+        const int64_t b = blockIdx.x, n = gridDim.x, x = b % kXcds;
+        const int64_t per = n / kXcds, rem = n % kXcds;
+        return x * per + (x < rem ? x : rem) + b / kXcds;
+    }();
     const int sub = (int)(item % p.nsub);
     const int grp = (int)((item / p.nsub) % p.G);
     const int64_t chunk = item / p.nsub / p.G;
@@ -361,6 +370,14 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     constexpr int TI = (4 * W + kBWaves - 1) / kBWaves;  // tile units per lane
     constexpr int SI = (kPGroup * N * (int)sizeof(T) / 1024 + kBWaves - 1) / kBWaves;  // state units
     u32x4 rx[TI], ry[TI], rg[SI], rh[SI];
+    // (carried chunk states) the span's states and this chunk's decays
+    u32x4 rgs[SI], rhs[SI];
+    float dgs = 0.f, dhs = 0.f;
+    const bool carried = p.hspan != nullptr;
+    // the chunk's four-chunk span
+    const int64_t span4 = !carried ? 0
+                          : p.nseq ? (int64_t)p.span_off4[p.table[chunk].x] + kc / 4
+                                   : (chunk / p.cps) * p.sps4 + kc / 4;
     auto tile_off = [&](int i, int64_t rstride) -> int64_t {
         const int j = (i % W) * 64 + lane;
         const int pr = j / W, pu = j % W;
@@ -391,6 +408,34 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
                 rh[k] = *(const u32x4*)((const T*)p.hprev + hb + o);
             }
         }
+        if (carried) {
+            const int64_t hs4 = (span4 * p.H + h) * (int64_t)P * N + (int64_t)pcol0 * N;
+#pragma unroll
+            for (int k = 0; k < SI; ++k) {
+                const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
+                if (o < PN) {
+                    rgs[k] = *(const u32x4*)((const T*)p.gspan + hs4 + o);
+                    rhs[k] = *(const u32x4*)((const T*)p.hspan + hs4 + o);
+                }
+            }
+            dgs = p.gdec[chunk * p.H + h];
+            dhs = p.hdec[chunk * p.H + h];
+        }
+    };
+    // a state entry run: the span-local part, plus the span's state times
+    // the decay between them (carried chunk states), in fp32
+    auto whole = [&](const u32x4& loc, const u32x4& sp, float dec) -> u32x4 {
+        if (!carried) return loc;
+        if constexpr (sizeof(T) == 2) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, loc), b = __builtin_bit_cast(bf16x8, sp);
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (bf16)(dec * (float)b[j] + (float)a[j]);
+            return __builtin_bit_cast(u32x4, o);
+        } else {
+            const f32x4 a = __builtin_bit_cast(f32x4, loc), b = __builtin_bit_cast(f32x4, sp);
+            return __builtin_bit_cast(u32x4, dec * b + a);
+        }
     };
     // One full wait, outside every branch: the prefetched registers are
     // needed now, and the compiler's wait placement then knows that nothing
@@ -419,8 +464,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
             const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
             if (o < kPGroup * N) {
                 const int so = srun(o / 4);  // the chunk's first run (EPU/4 runs, adjacent)
-                *(u32x4*)(sm.gr + so) = o < PN ? rg[k] : z;
-                *(u32x4*)(sm.hr + so) = o < PN ? rh[k] : z;
+                *(u32x4*)(sm.gr + so) = o < PN ? whole(rg[k], rgs[k], dgs) : z;
+                *(u32x4*)(sm.hr + so) = o < PN ? whole(rh[k], rhs[k], dhs) : z;
             }
         }
     };

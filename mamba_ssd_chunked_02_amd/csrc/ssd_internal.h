@@ -66,6 +66,17 @@ struct KParams {
                             // (varlen)
     const int32_t* chunk_slot;  // (varlen, chunk_out) first chunk slot of each
                                 // sequence
+    int32_t chunk_run;      // (chunk_out) the state is carried through the
+                            // span: chunk c's slot gets the span-local state
+                            // entering it (the chunks walked before it) and
+                            // its decay slot their decay product; the span's
+                            // whole local state and decay product go to
+                            // span_states / span_decay at slot span
+    int32_t walk_rev;       // (chunk_run) walk the span's chunks from its last
+                            // to its first (the output-gradient state, which
+                            // flows against the processing order)
+    void* span_states;      // (chunk_run) [nspan][H][P][N], input type
+    float* span_decay;      // (chunk_run) [nspan][H]
     int32_t state_f32;      // span states stored in float32 whatever the input
                             // type (span kernels, plans 0 and 1)
     float d_init;
@@ -81,6 +92,17 @@ struct BParams {
     const void* dy;         // dL/dy (strides gs_t, gs_h)
     const void* hprev;      // [nchunk][H][P*N] state entering each chunk
     const void* gout;       // [nchunk][H][P*N] dL/d(state leaving each chunk)
+    // With carried chunk states (hspan non-null) hprev and gout hold only
+    // the span-local parts: the state entering chunk c is hdec[c] times the
+    // state entering its four-chunk span (hspan) plus hprev[c], and the
+    // gradient of the state leaving it gdec[c] times the gradient of the
+    // state leaving the span (gspan) plus gout[c].
+    const void* hspan;      // [nspan4][H][P*N] or null
+    const void* gspan;      // [nspan4][H][P*N]
+    const float* hdec;      // [nchunk][H]
+    const float* gdec;      // [nchunk][H]
+    const int32_t* span_off4;  // (varlen) first four-chunk span of each sequence
+    int32_t sps4;           // (batch mode) four-chunk spans per sequence
     void* dx;               // [b, L, H, P], strided like x
     void* dd_raw;           // [b, L, H], strided like d_raw
     float* dB_part;         // [nsub][ntok][G][N] per head subset

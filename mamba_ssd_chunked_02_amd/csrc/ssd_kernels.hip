@@ -320,26 +320,30 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     const T* const bg = (const T*)p.B + (int64_t)grp * p.bs_g;
     const T* const cg = (const T*)p.C + (int64_t)grp * p.cs_g;
     const T* const dg = (const T*)p.d_raw + (int64_t)hc * p.ds_h;
-    // Row 0 of chunk c is token tb0 + c * dstep; its tokens left in the
-    // sequence are rem0 - 64c.
+    // Step c of the walk takes chunk ck(c) of the span: the span's chunks
+    // in order, or (a reversed chunk-state walk) from its last to its first.
+    // Row 0 of chunk k is token tb0 + k * dstep; its tokens left in the
+    // sequence are rem0 - 64k.
+    const bool wrev = is_state(MODE) && p.chunk_out && p.chunk_run && p.walk_rev;
+    auto ck = [&](int c) -> int { return wrev ? nck - 1 - c : c; };
     const int64_t cj0 = (int64_t)chunk0 * kChunk;
     const int64_t tb0 = start + (p.reverse ? len - 1 - cj0 : cj0);
     const int dstep = dir * kChunk;
     const int64_t rem0 = len - cj0;
-    auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(c * dstep); };
-    auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)c * kChunk); };
-    // chunk c's row-0 pointers: base at chunk 0 plus c chunk steps
+    auto tok0 = [&](int c) -> int64_t { return tb0 + (int64_t)(ck(c) * dstep); };
+    auto clen_of = [&](int c) -> int { return (int)imin(kChunk, rem0 - (int64_t)ck(c) * kChunk); };
+    // chunk k's row-0 pointers: base at chunk 0 plus k chunk steps
     const T* const xc0 = xg + tb0 * XS;
     const T* const bc0 = bg + tb0 * BS;
     const T* const cc0 = cg + tb0 * CS;
     const int64_t xcs = (int64_t)dstep * XS, bcs = (int64_t)dstep * BS, ccs = (int64_t)dstep * CS;
-    // Chunk c's X tile (wave w4 loads its own 16-column block) and this
+    // Step c's X tile (wave w4 loads its own 16-column block) and this
     // wave's share of the B tile.
     auto issue_xb = [&](int c, T* __restrict__ xdst, T* __restrict__ bdst) {
         const int cl = clen_of(c);
-        issue_tile<W, 1, XI>(xdst, xc0 + c * xcs, dir * XS, w4 * W, cl, pgw, lane);
-        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + c * bcs, dir * BS, wave, cl, N,
-                                                        lane);
+        issue_tile<W, 1, XI>(xdst, xc0 + ck(c) * xcs, dir * XS, w4 * W, cl, pgw, lane);
+        issue_tile<(BI + Cf::NW - 1) / Cf::NW, Cf::NW, BI>(bdst, bc0 + ck(c) * bcs, dir * BS, wave, cl,
+                                                        N, lane);
     };
     // This wave's share of chunk c's C tile (scan).
     auto issue_c = [&](int c, T* __restrict__ cdst) {
@@ -503,6 +507,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                             const T* __restrict__ ct, T* __restrict__ xn, T* __restrict__ bn,
                             T* __restrict__ cn) {
                 if (!last) issue_xb(c + 1, xn, bn);
+                if (!SCAN && chunk_out && p.chunk_run && active) {
+                    // (carried chunk states) the span-local state entering
+                    // this chunk: the chunks walked before it
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        store4_async(state_ptr(slot0 + ck(c)) + state_off(pb, nb, lane, NB), Hs[nb]);
+                }
 
                 if constexpr (SCAN) {
                     // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
@@ -620,7 +631,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                     }
                 }
                 if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
-                if (!SCAN && chunk_out) {
+                if (!SCAN && chunk_out && !p.chunk_run) {
                     // this chunk's local state; the next starts from zero
                     if (active) {
 #pragma unroll
@@ -637,10 +648,27 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
     if constexpr (is_state(MODE)) {
         run(std::false_type{});
-        if (chunk_out) {
+        if (chunk_out && !p.chunk_run) {
             // chunk w4's decay (its factors are still in slot w4: K <= 4)
             if (pg == 0 && w4 < nck && live && lane == 0)
                 p.decay[(slot0 + w4) * p.H + h] = fexp2(sm.dec[w4][q].cs2[kChunk - 1]);
+            return;
+        }
+        if (chunk_out) {
+            // (carried chunk states) walk step w4's decay slot: the decay
+            // product of the steps before it (their factors are still in
+            // slots 0..3: K <= 4); the span's whole local state and decay
+            if (pg == 0 && w4 < nck && live && lane == 0) {
+                float l2 = 0.f;
+                for (int j = 0; j < w4; ++j) l2 += sm.dec[j][q].cs2[kChunk - 1];
+                p.decay[(slot0 + ck(w4)) * p.H + h] = fexp2(l2);
+            }
+            if (active) {
+                T* const sp = (T*)p.span_states + (span * p.H + h) * (int64_t)p.P * N;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) store4(sp + state_off(pb, nb, lane, NB), Hs[nb]);
+            }
+            if (pg == 0 && w4 == 0 && live && lane == 0) p.span_decay[span * p.H + h] = fexp2(logdec2);
             return;
         }
         if (active) {
