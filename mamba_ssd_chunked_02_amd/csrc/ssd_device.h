@@ -280,6 +280,16 @@ struct __attribute__((aligned(16))) Decay {  // read with 16-byte vector loads
     float fm[8];        // block pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
 };
 
+// The factors a chunk-state pass needs (a quarter of Decay's LDS): the
+// cumulative log-decay and the state update weights -- 2^{cs_last - cs_s} d_s,
+// or 2^{cs_s} (0 past the end) for the output-gradient states.
+struct __attribute__((aligned(16))) DecayS {
+    float cs2[kChunk];
+    float w[kChunk];
+};
+__device__ __forceinline__ float chunk_decay(const Decay& D) { return D.fe[kChunk - 1]; }
+__device__ __forceinline__ float chunk_decay(const DecayS& D) { return fexp2(D.cs2[kChunk - 1]); }
+
 // Span states are kept in MFMA result order so each wave moves 64 contiguous
 // 4-value groups: within one (span, head) block of P*N values, state entry
 // (n, p) with p = 16*pb + l, n = 16*nb + 4*g + i sits at
@@ -313,6 +323,15 @@ __device__ __forceinline__ void decay_factors(Decay& D, uint32_t raw, float d_in
         const float cs = (lane == 0 || lane == 1 || lane == 3) ? c1 : ((lane == 2 || lane == 4) ? c2 : c3);
         D.fm[lane] = fexp2(ct - cs);
     }
+}
+template <typename T>
+__device__ __forceinline__ void decay_factors(DecayS& D, uint32_t raw, float d_init, int clen,
+                                              int lane, bool grad) {
+    const float draw = __uint_as_float(sizeof(T) == 2 ? raw << 16 : raw);
+    const float dt = lane < clen ? softplus(draw + d_init) : 0.f;
+    const float v = wave_prefix_sum(-dt * kLog2e);
+    D.cs2[lane] = v;
+    D.w[lane] = grad ? (lane < clen ? fexp2(v) : 0.f) : fexp2(lane_value(v, 63) - v) * dt;
 }
 
 }  // namespace

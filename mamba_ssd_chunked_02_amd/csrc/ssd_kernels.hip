@@ -70,6 +70,11 @@ __device__ __forceinline__ constexpr int lslot(int tb, int kk) {
 }
 
 
+// v itself, as an expression that depends on the tag's type: uses of v
+// inside `if constexpr` on the tag are then checked only where taken.
+template <typename Tag, typename V>
+__device__ __forceinline__ const V& dep_on(Tag, const V& v) { return v; }
+
 // LDS of one span workgroup.  X and B tiles are double-buffered: chunk
 // c+1's fill one buffer while chunk c is computed from the other.  The C tile
 // has one buffer, refilled as soon as the step's C reads are done.  Decay
@@ -85,7 +90,9 @@ struct __attribute__((aligned(16))) Smem {
     // contiguous run of 64 8-byte (bf16) values, so writes and reads of one
     // half never share a bank
     X4 lf[SCAN ? HG : 1][SCAN ? 6 : 1][2][SCAN ? 64 : 1];
-    Decay dec[kWaves][HG];              // chunk 4b + w of the current batch b, per head
+    // chunk 4b + w of the current batch b, per head (a state pass keeps only
+    // what its update needs)
+    std::conditional_t<SCAN, Decay, DecayS> dec[kWaves][HG];
     __attribute__((aligned(16))) uint32_t dr[2][kWaves][HG][kChunk];  // d_raw of a batch, per lane
     uint32_t ticket, epoch;  // fused kernel: this workgroup's ticket and epoch
 };
@@ -452,6 +459,17 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     // flight.
     auto run = [&](auto scan_tag) __attribute__((always_inline)) {
         constexpr bool SCAN = decltype(scan_tag)::value;
+        // a chunk's decay factors, and the state update weights among them
+        auto form_dec = [&](auto& D, uint32_t raw, int cl) {
+            if constexpr (std::is_same_v<std::decay_t<decltype(D)>, DecayS>)
+                decay_factors<T>(D, raw, p.d_init, cl, lane, MODE == kModeStateGrad);
+            else
+                decay_factors<T>(D, raw, p.d_init, cl, lane);
+        };
+        auto state_w = [&](const auto& D, int s0) -> const float* {
+            if constexpr (std::is_same_v<std::decay_t<decltype(D)>, DecayS>) return &D.w[s0];
+            else return MODE == kModeStateGrad ? &D.fe[s0] : &D.w[s0];
+        };
         if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
         if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
         issue_xb(0, sm.xs[0][q], sm.bs[0]);
@@ -478,13 +496,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                 fold_apply();
             }
         }
-        if (w4 < nck) decay_factors<T>(sm.dec[w4][q], sm.dr[0][w4][q][lane], p.d_init, clen_of(w4), lane);
+        if (w4 < nck) form_dec(sm.dec[w4][q], sm.dr[0][w4][q][lane], clen_of(w4));
 
         for (int c = 0; c < nck; ++c) {
             const bool last = c + 1 == nck;
             const int buf = c & 1;
             const int cl = clen_of(c);
-            const Decay& D = sm.dec[c % kWaves][q];
+            const auto& D = sm.dec[c % kWaves][q];
 
             // After chunk c's loads this wave issued, in an active scan wave,
             // exactly four y stores (the previous chunk is full), else nothing.
@@ -498,7 +516,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                 // batch c/4: its d_raw was loaded four steps ago
                 const int bb = (c / kWaves) & 1;
                 if (c + w4 < nck)
-                    decay_factors<T>(sm.dec[w4][q], sm.dr[bb][w4][q][lane], p.d_init, clen_of(c + w4), lane);
+                    form_dec(sm.dec[w4][q], sm.dr[bb][w4][q][lane], clen_of(c + w4));
                 block_sync();
                 if (c + kWaves + w4 < nck) issue_d(c + kWaves + w4, sm.dr[bb ^ 1][w4][q]);
             }
@@ -516,6 +534,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                 }
 
                 if constexpr (SCAN) {
+                    const auto& Ds = dep_on(scan_tag, D);  // the scan's full factor set
                     // C rows 16*tb + l16, the B operand of C B^T and H^T C^T
                     X8 cf[4][KN];
 #pragma unroll
@@ -553,27 +572,27 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                     switch (w4) {
                         case 0:
                             bfrag(0);
-                            mask_tile<0, 0>(sm, D, q, lane, a, cf[0]);
-                            mask_tile<1, 0>(sm, D, q, lane, a, cf[1]);
-                            mask_tile<2, 0>(sm, D, q, lane, a, cf[2]);
+                            mask_tile<0, 0>(sm, Ds, q, lane, a, cf[0]);
+                            mask_tile<1, 0>(sm, Ds, q, lane, a, cf[1]);
+                            mask_tile<2, 0>(sm, Ds, q, lane, a, cf[2]);
                             break;
                         case 1:
                             bfrag(1);
-                            mask_tile<1, 1>(sm, D, q, lane, a, cf[1]);
-                            mask_tile<2, 1>(sm, D, q, lane, a, cf[2]);
-                            mask_tile<3, 1>(sm, D, q, lane, a, cf[3]);
+                            mask_tile<1, 1>(sm, Ds, q, lane, a, cf[1]);
+                            mask_tile<2, 1>(sm, Ds, q, lane, a, cf[2]);
+                            mask_tile<3, 1>(sm, Ds, q, lane, a, cf[3]);
                             break;
                         case 2:
                             bfrag(0);
-                            mask_tile<3, 0>(sm, D, q, lane, a, cf[3]);
+                            mask_tile<3, 0>(sm, Ds, q, lane, a, cf[3]);
                             bfrag(2);
-                            mask_tile<2, 2>(sm, D, q, lane, a, cf[2]);
+                            mask_tile<2, 2>(sm, Ds, q, lane, a, cf[2]);
                             break;
                         default:
                             bfrag(2);
-                            mask_tile<3, 2>(sm, D, q, lane, a, cf[3]);
+                            mask_tile<3, 2>(sm, Ds, q, lane, a, cf[3]);
                             bfrag(3);
-                            mask_tile<3, 3>(sm, D, q, lane, a, cf[3]);
+                            mask_tile<3, 3>(sm, Ds, q, lane, a, cf[3]);
                             break;
                     }
                     block_sync();  // masked fragments complete, C tile no longer read
@@ -595,7 +614,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                         f32x4 yi = mma(xf[0], lf[lslot(tb, 0)], z);
                         if (tb >= 2) yi = mma(xf[1], lf[lslot(tb, 1)], yi);
                         const int t = 16 * tb + l16;
-                        const float sc = D.fe[t];
+                        const float sc = Ds.fe[t];
                         f32x4 o;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) o[i] = yi[i] + sc * ye[tb][i];
@@ -605,13 +624,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
                 if (!(SCAN && last) || (SCAN && write_final)) {
                     // advance the state over this chunk: H = e^{cs_last} H + B^T (w X)
-                    const float decay = D.fe[kChunk - 1];
+                    const float decay = chunk_decay(D);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) Hs[nb] *= decay;
 #pragma unroll
                     for (int kk = 0; kk < kChunk / 32; ++kk) {
                         const int s0 = 32 * kk + 8 * g;  // tokens s0 .. s0+7
-                        f32x8 ws = ld8(MODE == kModeStateGrad ? &D.fe[s0] : &D.w[s0]);
+                        f32x8 ws = ld8(state_w(D, s0));
                         if constexpr (MODE == kModeStateGrad) {
                             // e^{cs_s} does not vanish past a partial chunk's
                             // end (d_s does): rows there hold row 0 again
