@@ -264,21 +264,40 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     }
     // (the host keeps span x head group x column group below 2^31, so the
     // decode divides in 32 bits)
-    const uint32_t lg32 = (uint32_t)logical, rest = lg32 / (uint32_t)p.npg;
-    const int pg = (int)(lg32 - rest * (uint32_t)p.npg);
-    uint32_t span32 = rest / (uint32_t)ngrp;
-    const int hgi = (int)(rest - span32 * (uint32_t)ngrp);
-    if (MODE != kModeFused && !p.nseq && p.batch > 1) {
-        // Interleave the sequences' spans, each odd sequence's in reverse
-        // order: neighbouring logical spans (one XCD) then pair early and
-        // late positions, so the XCDs share the fold's re-reads of earlier
-        // span states evenly instead of one XCD holding every late span.
-        // Within a pair the later position (the longer fold) comes first:
-        // an XCD's first workgroups each get a CU of their own.
-        const uint32_t B = (uint32_t)p.batch, S = (uint32_t)p.sps;
-        const uint32_t k = span32 / B, j = span32 % B;
-        const uint32_t sq = 2u * k < S ? B - 1u - j : j;
-        span32 = sq * S + ((sq & 1u) ? S - 1u - k : k);
+    int pg, hgi;
+    uint32_t span32;
+    const uint32_t nchain = (uint32_t)p.batch * (uint32_t)ngrp * (uint32_t)p.npg;
+    if ((MODE == kModeScan || (MODE == kModeState && !p.chunk_out)) && p.fuse_pass == 1 &&
+        !p.nseq && nchain % kXcds == 0) {
+        // A scan that folds the earlier span states itself, and the state
+        // launch before it: each XCD takes whole chains (sequence, head
+        // group, column group), every span of them, so the fold's re-reads
+        // of a chain's span states meet in one L2 (the XCD that formed them)
+        // and each XCD folds the same amount.  Later positions (longer
+        // folds) are dealt first: an XCD's first workgroups each get a CU of
+        // their own.
+        const uint32_t S = (uint32_t)p.sps, cpx = nchain / kXcds;
+        const uint32_t x = (uint32_t)(blk % kXcds), slot = (uint32_t)(blk / kXcds);
+        const uint32_t pr = slot / cpx, chain = x * cpx + (slot - pr * cpx);
+        const uint32_t rest = chain / (uint32_t)p.npg;
+        pg = (int)(chain - rest * (uint32_t)p.npg);
+        const uint32_t seq = rest / (uint32_t)ngrp;
+        hgi = (int)(rest - seq * (uint32_t)ngrp);
+        span32 = seq * S + (S - 1u - pr);
+    } else {
+        const uint32_t lg32 = (uint32_t)logical, rest = lg32 / (uint32_t)p.npg;
+        pg = (int)(lg32 - rest * (uint32_t)p.npg);
+        span32 = rest / (uint32_t)ngrp;
+        hgi = (int)(rest - span32 * (uint32_t)ngrp);
+        if (MODE != kModeFused && !p.nseq && p.batch > 1) {
+            // Interleave the sequences' spans, each odd sequence's in reverse
+            // order: neighbouring logical spans (one XCD) then pair an early
+            // and a late position, the later one first.
+            const uint32_t B = (uint32_t)p.batch, S = (uint32_t)p.sps;
+            const uint32_t k = span32 / B, j = span32 % B;
+            const uint32_t sq = 2u * k < S ? B - 1u - j : j;
+            span32 = sq * S + ((sq & 1u) ? S - 1u - k : k);
+        }
     }
     const int64_t span = span32;
     const int h0 = hgi * hg;
