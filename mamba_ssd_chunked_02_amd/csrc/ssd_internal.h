@@ -13,6 +13,7 @@ constexpr int kWaves = 4;      // wavefronts per workgroup in the span kernels
 constexpr int kThreads = 256;  // kWaves * 64
 constexpr int kPGroup = 64;    // headdim columns per workgroup (16 per wave)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kXcdCus = 32;    // MI355X: 32 CUs per XCD
 
 // Everything the kernels need, passed by value.
 struct KParams {

@@ -273,12 +273,24 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         // launch before it: each XCD takes whole chains (sequence, head
         // group, column group), every span of them, so the fold's re-reads
         // of a chain's span states meet in one L2 (the XCD that formed them)
-        // and each XCD folds the same amount.  Later positions (longer
-        // folds) are dealt first: an XCD's first workgroups each get a CU of
-        // their own.
+        // and each XCD folds the same amount.  Ranked by fold length (rank
+        // 0: the last position), the workgroups are placed so that the
+        // longest folds get a CU of their own: with n workgroups on an
+        // XCD's c CUs (c < n <= 2c), slots j and j + c (j < n - c) share a
+        // CU and slots n - c .. c - 1 run alone; the alone slots take the
+        // first 2c - n ranks, and each shared CU pairs the next heaviest
+        // rank with the lightest one left.
         const uint32_t S = (uint32_t)p.sps, cpx = nchain / kXcds;
         const uint32_t x = (uint32_t)(blk % kXcds), slot = (uint32_t)(blk / kXcds);
-        const uint32_t pr = slot / cpx, chain = x * cpx + (slot - pr * cpx);
+        const uint32_t n = S * cpx, c = kXcdCus;
+        uint32_t rank = slot;
+        if (n > c && n <= 2 * c) {
+            const uint32_t np = n - c;  // CUs holding two
+            if (slot >= np && slot < c) rank = slot - np;
+            else if (slot < np) rank = (2 * c - n) + slot;
+            else rank = n - 1 - (slot - c);
+        }
+        const uint32_t pr = rank / cpx, chain = x * cpx + (rank - pr * cpx);
         const uint32_t rest = chain / (uint32_t)p.npg;
         pg = (int)(chain - rest * (uint32_t)p.npg);
         const uint32_t seq = rest / (uint32_t)ngrp;
