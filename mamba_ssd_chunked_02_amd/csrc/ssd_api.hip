@@ -44,9 +44,15 @@ const ssd_tuning kNoTuning = {};
 // walked by one workgroup, so spans stay short enough to keep the grid wide.
 // Four-chunk spans, or eight when that still leaves >= 2048 span x
 // head-group items (8192 tokens x 80 heads: 8-chunk spans run 15 % faster).
-int32_t choose_k(int64_t nch, int64_t groups) {
+// A grid narrower than the chip's 256 CUs takes shorter spans (fewer chunk
+// steps in a row, more workgroups), down to one chunk, as long as a sequence
+// keeps at most eight spans so the scan still folds them itself (256 tokens
+// x 2 heads: 11.3 us with one-chunk spans, 22.4 with four).  cps: chunks per
+// sequence, 0 for packed sequences.
+int32_t choose_k(int64_t nch, int64_t groups, int64_t cps) {
     int32_t K = 4;
     while (K < 8 && ceil_div(nch, K) * groups >= 2048) K *= 2;
+    while (K > 1 && cps > 0 && ceil_div(nch, K) * groups < 256 && ceil_div(cps, K / 2) <= 8) K /= 2;
     return K;
 }
 
@@ -120,7 +126,8 @@ int make_plan(const ssd_dims* d, const ssd_tuning* tun, Plan* pl) {
     const int64_t nch_bound = d->nseq > 0 ? ceil_div(T, kChunk) + d->nseq
                                           : (int64_t)d->batch * ceil_div(d->seqlen, kChunk);
     pl->K = t.chunks_per_span ? t.chunks_per_span
-                              : choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg);
+                              : choose_k(nch_bound, ceil_div(d->nheads, pl->hg_scan) * pl->npg,
+                                         d->nseq > 0 ? 0 : ceil_div(d->seqlen, kChunk));
     // Large bf16 problems with d_state 64 or 128 run the head-wave kernels.
     bool hw = false;
     if (hw_ok && !t.state_f32) {
