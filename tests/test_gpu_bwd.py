@@ -89,12 +89,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("chunks", [1, 4])
 @pytest.mark.parametrize("rev", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_bwd_shapes_bf16(ssd, shape, rev):
+def test_bwd_shapes_bf16(ssd, shape, rev, chunks):
+    """Every shape with both chunk-state plans (small problems default to
+    one chunk per chunk-state workgroup)."""
     b, L, H, P, N, G = shape
     p = random_problem(301, b, L, H, P, N, ngroups=G, dtype="bf16", init_scale=0.5, d_init=-2.0)
-    bwd_case(ssd, p, reverse=rev, label=f"bwd {shape} rev={rev}")
+    bwd_case(ssd, p, reverse=rev, label=f"bwd {shape} rev={rev} chunks={chunks}",
+             tuning={"bwd_state_chunks": chunks})
 
 
 @pytest.mark.parametrize("N", [16, 32])
@@ -177,22 +181,24 @@ def test_bwd_strided_dy_and_y(ssd):
         assert F.rel_err(got[k].float().cpu(), ref[k]) <= BWD_TOL[torch.bfloat16], k
 
 
-def test_bwd_long_walks_weak_decay(ssd):
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_bwd_long_walks_weak_decay(ssd, chunks):
     """Both chunk-state passes over walks of 1 to 38 chunks (every position of
     the pass's two batches of eight in flight, walks past two batches), with
     weak decay so a state carried wrongly anywhere shows in the gradients of
-    the sequence's first tokens and of the initial state."""
+    the sequence's first tokens and of the initial state; with one chunk per
+    chunk-state workgroup, and with four-chunk spans whose states are carried
+    (the last span of a sequence shorter, its last chunk ragged)."""
+    t = {"bwd_state_chunks": chunks}
     lens = [64 * 37 + 5, 64 * 16, 1, 64 * 17 - 3, 64 * 9]
     p = random_problem(347, 1, 0, 2, 16, 16, dtype="f32", lengths=lens, d_init=-6.0,
                        init_scale=1.0)
-    bwd_case(ssd, p, label="bwd long walks")
-    bwd_case(ssd, p, reverse=True, label="bwd long walks rev")
-    # batch mode: the chunk states come from workgroups that walk four chunks
-    # each (the last span of a sequence shorter, its last chunk ragged)
+    bwd_case(ssd, p, label="bwd long walks", tuning=t)
+    bwd_case(ssd, p, reverse=True, label="bwd long walks rev", tuning=t)
     q = random_problem(349, 2, 64 * 37 + 5, 2, 16, 16, dtype="f32", d_init=-6.0,
                        init_scale=1.0)
-    bwd_case(ssd, q, label="bwd long batch")
-    bwd_case(ssd, q, reverse=True, label="bwd long batch rev")
+    bwd_case(ssd, q, label="bwd long batch", tuning=t)
+    bwd_case(ssd, q, reverse=True, label="bwd long batch rev", tuning=t)
 
 
 
