@@ -224,6 +224,17 @@ def forward_calls(m, w, d, dev):
     return calls, ycat
 
 
+def step_calls(m, w, d, calls, ycat):
+    """What one timed forward step launches: the prepared calls, or for the
+    bidirectional workload one ssd_fwd_bidir call into the same [b, L, H, 2P]
+    output (both directions' span states from one pass where the spans
+    allow).  ``calls`` stay the per-direction calls that single stages are
+    timed with."""
+    if not w.bidir:
+        return calls
+    return [m.prepare_bidir(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], y=ycat)]
+
+
 def backward_calls(m, w, d, dev, calls, ycat):
     """The prepared ssd_bwd calls of one step, for a seeded dL/dy (and dL/d
     final_state); [] where the backward is not built for these sizes."""
@@ -320,10 +331,11 @@ def workload_line(m, name: str, dev, with_bwd: bool) -> dict:
     w = by_name(name)
     _, d = load_workload(w, dev)
     calls, ycat = forward_calls(m, w, d, dev)
+    scalls = step_calls(m, w, d, calls, ycat)
     plan = m.ssd_fwd_plan(calls[0].dims)
     big = w.tokens >= (1 << 20)
     steps, warm = (3, 1) if big else (20, 3)
-    fwd = wall_ms(lambda: [c.run() for c in calls], steps, warm)
+    fwd = wall_ms(lambda: [c.run() for c in scalls], steps, warm)
     stages = plan_stages(m, w, plan)
     us = stage_times_us(m, calls, stages, 2 if big else 10)
     used = spans_used(w, plan, d["cu_seqlens"])
@@ -349,7 +361,7 @@ def workload_line(m, name: str, dev, with_bwd: bool) -> dict:
             line["bwd_ms_per_step"] = round(bwd, 5)
             line["bwd_mtokens_per_s"] = round(w.tokens / (bwd * 1e-3) / 1e6, 3)
         del bcalls
-    del calls, ycat, d
+    del calls, scalls, ycat, d
     torch.cuda.empty_cache()
     return line
 
@@ -388,6 +400,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     host, d = load_workload(w, dev)
     calls, ycat = forward_calls(m, w, d, dev)
+    scalls = step_calls(m, w, d, calls, ycat)
     plan = m.ssd_fwd_plan(calls[0].dims)
     stream = torch.cuda.current_stream(dev)
     if args.copy_mib:
@@ -399,7 +412,7 @@ def main() -> int:
         del src, dst
 
     def step():
-        for c in calls:
+        for c in scalls:
             c.run()
 
     # timed region: exactly K steps, caches warm

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 7
+#define SSD_ABI_VERSION 8
 
 /* Status codes: 0 is success, every error is negative. */
 enum {
@@ -256,6 +256,34 @@ int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuni
                void* y, float* final_state,
                void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * Both directions of the bidirectional mode (jsqmd.com page §3.1: the
+ * causal scan and the same scan over the time-flipped sequence, their
+ * outputs concatenated) in one call, batch mode only (no cu_seqlens):
+ * y_fwd, final_fwd are ssd_fwd's outputs with reverse = 0 from init_fwd,
+ * y_rev, final_rev those with reverse = 1 from init_rev.  Both outputs
+ * follow layout's y strides (for example the two halves of one
+ * [b, L, H, 2P] tensor).  Arguments and checks otherwise as ssd_fwd_ex
+ * with every stage; either direction's error is returned before anything
+ * is queued.  Where every span of a sequence is whole (L a multiple of
+ * 64 times ssd_fwd_plan's chunks_per_span) and the plan keeps a separate
+ * state stage (fused_pass 0 or 1), the span states of both directions are
+ * formed in one pass over x, B and d_raw; otherwise the two directions run
+ * as two ssd_fwd_ex calls.  Each output agrees with the one-direction
+ * call's to rounding (the states are accumulated in another order).
+ *   workspace   at least ssd_fwd_bidir_workspace_bytes(dims) bytes (two
+ *               forward workspaces), 256-byte aligned, no initialization
+ */
+size_t ssd_fwd_bidir_workspace_bytes(const ssd_dims* dims);
+
+int ssd_fwd_bidir(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout* layout,
+                  const void* x, const void* d_raw, float d_init,
+                  const void* B, const void* C,
+                  const float* init_fwd, const float* init_rev,
+                  void* y_fwd, void* y_rev, float* final_fwd, float* final_rev,
+                  void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * Backward pass: the gradients of a loss L with respect to every input of

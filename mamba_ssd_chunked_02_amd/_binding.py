@@ -133,6 +133,16 @@ def library() -> ctypes.CDLL:
         lib.ssd_fwd_ex.restype = ctypes.c_int
         lib.ssd_fwd_ex.argtypes = [ctypes.c_uint32, ctypes.POINTER(SsdDims),
                                    ctypes.POINTER(SsdTuning)] + fwd_args[1:]
+        lib.ssd_fwd_bidir_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_fwd_bidir_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims)]
+        lib.ssd_fwd_bidir.restype = ctypes.c_int
+        lib.ssd_fwd_bidir.argtypes = [
+            ctypes.POINTER(SsdDims), ctypes.POINTER(SsdTuning), ctypes.POINTER(SsdLayout),
+            P_, P_, ctypes.c_float, P_, P_,
+            P_, P_, P_, P_, P_, P_,
+            P_, ctypes.c_size_t,
+            P_,
+        ]
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_plan.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(SsdTuning),
                                      ctypes.POINTER(SsdPlanInfo)]
@@ -364,14 +374,102 @@ def ssd_fwd_noalloc_max_bytes() -> int:
     return int(library().ssd_fwd_noalloc_max_bytes())
 
 
+class PreparedBidir:
+    """Marshalled arguments of one ssd_fwd_bidir call (tensors kept alive)."""
+
+    def __init__(self, dims, tuning, layout, args, keep, y, finals, workspace):
+        self.dims = dims
+        self.tuning = tuning
+        self.layout = layout
+        self.args = args
+        self._keep = keep
+        self.y = y
+        self.final_states = finals
+        self.workspace = workspace
+
+    def run(self, stream=None):
+        """Launch both directions on ``stream`` (torch's current stream of
+        the tensors' device by default)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.y.device).cuda_stream
+        t = None if self.tuning is None else ctypes.byref(self.tuning)
+        rc = library().ssd_fwd_bidir(ctypes.byref(self.dims), t, ctypes.byref(self.layout),
+                                     *self.args, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise SsdError(rc, "ssd_fwd_bidir")
+        return self.y, self.final_states
+
+
+def prepare_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_fwd=None, init_rev=None,
+                  y=None, final_state=False, workspace=None, tuning=None) -> PreparedBidir:
+    """Check and marshal the arguments of ``ssd_fwd_bidir`` (batch mode): the
+    forward output goes to y[..., :P] and the reverse one to y[..., P:] of a
+    [b,L,H,2P] tensor (allocated when not given); ``final_state=True``
+    allocates both final states, or pass a (final_fwd, final_rev) pair."""
+    if x.dim() != 4 or d_raw.dim() != 3 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("x [b,L,H,P], d_raw [b,L,H], B/C [b,L,G,N] expected")
+    b, L, H, P = x.shape
+    dev = x.device
+    for name, t in (("d_raw", d_raw), ("B", B), ("C", C)):
+        if t.device != dev or t.dtype != x.dtype:
+            raise ValueError(f"{name} must be on {dev} with dtype {x.dtype}")
+    if tuple(d_raw.shape) != (b, L, H) or tuple(B.shape[:2]) != (b, L) or B.shape != C.shape:
+        raise ValueError("shape mismatch between x, d_raw, B and C")
+    N = B.shape[3]
+    for name, st in (("init_fwd", init_fwd), ("init_rev", init_rev)):
+        if st is not None and (st.dtype != torch.float32 or tuple(st.shape) != (b, H, N, P)
+                               or st.device != dev or not st.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [{b},{H},{N},{P}] on {dev}")
+    if y is None:
+        y = torch.empty((b, L, H, 2 * P), dtype=x.dtype, device=dev)
+    elif tuple(y.shape) != (b, L, H, 2 * P) or y.dtype != x.dtype or y.device != dev:
+        raise ValueError("y must be [b,L,H,2P] with x's dtype and device")
+    if final_state is True:
+        finals = tuple(torch.empty((b, H, N, P), dtype=torch.float32, device=dev) for _ in range(2))
+    elif final_state is False or final_state is None:
+        finals = (None, None)
+    else:
+        finals = tuple(final_state)
+        for f in finals:
+            if f is not None and (tuple(f.shape) != (b, H, N, P) or f.dtype != torch.float32
+                                  or not f.is_contiguous()):
+                raise ValueError(f"final states must be contiguous float32 [{b},{H},{N},{P}]")
+    dims = dims_for(x, B, chunk_size, None)
+    yf, yr = y[..., :P], y[..., P:]
+    lay = layout_of(x, d_raw, B, C, yf)
+    tun = make_tuning(tuning)
+    if workspace is None:
+        if tun is None:
+            need = int(library().ssd_fwd_bidir_workspace_bytes(ctypes.byref(dims)))
+        else:
+            info = SsdPlanInfo()
+            rc = library().ssd_fwd_plan(ctypes.byref(dims), ctypes.byref(tun), ctypes.byref(info))
+            need = 2 * ((info.workspace_bytes + 255) // 256 * 256) if rc == 0 else 0
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = (_ptr(x), _ptr(d_raw), float(d_init), _ptr(B), _ptr(C),
+            _ptr(init_fwd), _ptr(init_rev), _ptr(yf), _ptr(yr), _ptr(finals[0]), _ptr(finals[1]),
+            _ptr(workspace), workspace.numel())
+    keep = (x, d_raw, B, C, init_fwd, init_rev, yf, yr)
+    return PreparedBidir(dims, tun, lay, args, keep, y, finals, workspace)
+
+
 def ssd_fwd_bidir(x, d_raw, d_init, B, C, chunk_size=CHUNK, init_state=None,
                   cu_seqlens=None, final_state=False, workspace=None, tuning=None):
     """Bidirectional scan: a forward pass and a reverse pass over the same
     inputs, outputs concatenated on the last dim -> y [b,L,H,2P].  The
     reverse pass runs each sequence from its end to its start and writes at
-    each token's own position, so no flipped copies are made.
+    each token's own position, so no flipped copies are made.  Both passes
+    start from init_state.  Without cu_seqlens this is one ssd_fwd_bidir call
+    (which forms both directions' span states in one pass where the spans
+    allow); with them, two ssd_fwd calls.
     Returns (y, (final_fwd, final_rev) or None)."""
     b, L, H, P = x.shape
+    if cu_seqlens is None:
+        call = prepare_bidir(x, d_raw, d_init, B, C, chunk_size, init_state, init_state,
+                             final_state=final_state, workspace=workspace, tuning=tuning)
+        with torch.cuda.device(x.device):
+            y, finals = call.run()
+        return y, (finals if final_state else None)
     y = torch.empty((b, L, H, 2 * P), dtype=x.dtype, device=x.device)
     c0 = prepare(x, d_raw, d_init, B, C, chunk_size, init_state, cu_seqlens, False,
                  y=y[..., :P], final_state=final_state, workspace=workspace, tuning=tuning)

@@ -469,11 +469,14 @@ int ssd_fwd(const ssd_dims* dims, const ssd_layout* layout, const void* x, const
                       cu_seqlens, reverse, y, final_state, workspace, workspace_bytes, stream);
 }
 
-int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
-               const ssd_layout* layout, const void* x, const void* d_raw, float d_init,
-               const void* B, const void* C, const float* init_state, const int32_t* cu_seqlens,
-               int32_t reverse, void* y, float* final_state, void* workspace,
-               size_t workspace_bytes, void* stream) {
+// The forward call.  With rev_ws, the state stage forms both directions' span
+// states in one launch: the reverse pass's into rev_ws, a workspace of the
+// same plan (only whole spans in batch mode; the caller checks).
+static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
+                    const ssd_layout* layout, const void* x, const void* d_raw, float d_init,
+                    const void* B, const void* C, const float* init_state,
+                    const int32_t* cu_seqlens, int32_t reverse, void* y, float* final_state,
+                    void* workspace, size_t workspace_bytes, void* stream, char* rev_ws) {
     if (mask & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_SHAPE;
     Plan pl;
     const int st = make_plan(dims, tuning, &pl);
@@ -567,8 +570,16 @@ int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
         }
     }
     if ((mask & SSD_STAGE_STATE) && pl.fuse != 2) {
-        e = pl.hw_npb ? ssd::launch_hw_state(p, d.d_state, s)
-                      : ssd::launch_span_state(p, d.dtype, d.d_state, s);
+        if (rev_ws) {
+            ssd::KParams pj = p;
+            pj.hg_state = 1;
+            pj.rev_states = rev_ws + pl.off_states;
+            pj.rev_decay = (float*)(rev_ws + pl.off_decay);
+            e = ssd::launch_span_state_both(pj, d.dtype, d.d_state, s);
+        } else {
+            e = pl.hw_npb ? ssd::launch_hw_state(p, d.d_state, s)
+                          : ssd::launch_span_state(p, d.dtype, d.d_state, s);
+        }
         if (e != hipSuccess) return SSD_ERR_HIP;
     }
     if ((mask & SSD_STAGE_PASS) && !pl.fuse) {
@@ -584,6 +595,61 @@ int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
         e = pl.hw_npb ? ssd::launch_hw_scan(p, d.d_state, s)
                       : ssd::launch_span_scan(p, d.dtype, d.d_state, s);
         if (e != hipSuccess) return SSD_ERR_HIP;
+    }
+    return SSD_OK;
+}
+
+int ssd_fwd_ex(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tuning,
+               const ssd_layout* layout, const void* x, const void* d_raw, float d_init,
+               const void* B, const void* C, const float* init_state, const int32_t* cu_seqlens,
+               int32_t reverse, void* y, float* final_state, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    return fwd_impl(mask, dims, tuning, layout, x, d_raw, d_init, B, C, init_state, cu_seqlens,
+                    reverse, y, final_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t ssd_fwd_bidir_workspace_bytes(const ssd_dims* dims) {
+    Plan pl;
+    if (make_plan(dims, nullptr, &pl) != SSD_OK) return 0;
+    return 2 * align_up(pl.total);
+}
+
+int ssd_fwd_bidir(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layout* layout,
+                  const void* x, const void* d_raw, float d_init, const void* B, const void* C,
+                  const float* init_fwd, const float* init_rev, void* y_fwd, void* y_rev,
+                  float* final_fwd, float* final_rev, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    Plan pl;
+    const int st = make_plan(dims, tuning, &pl);
+    if (st != SSD_OK) return st;
+    const size_t half = align_up(pl.total);
+    if (half > 0 && (!workspace || workspace_bytes < 2 * half)) return SSD_ERR_WORKSPACE;
+    char* const wf = (char*)workspace;
+    char* const wr = half > 0 ? wf + half : nullptr;
+    // both calls checked before anything is launched (an empty stage mask)
+    for (int r = 0; r < 2; ++r) {
+        const int c = ssd_fwd_ex(0, dims, tuning, layout, x, d_raw, d_init, B, C,
+                                 r ? init_rev : init_fwd, nullptr, r, r ? y_rev : y_fwd,
+                                 r ? final_rev : final_fwd, r ? wr : wf, half, stream);
+        if (c != SSD_OK) return c;
+    }
+    // One state launch for both directions where their spans cover the same
+    // tokens (whole spans) and the plan keeps a separate state stage.
+    const ssd_dims& d = *dims;
+    const bool joint = d.nseq == 0 && d.seqlen > 0 && pl.fuse != 2 &&
+                       d.seqlen % ((int64_t)kChunk * pl.K) == 0 &&
+                       (d.d_state == 16 || d.d_state == 32 || d.d_state == 64 || d.d_state == 128);
+    const uint32_t rest = joint ? (uint32_t)(SSD_STAGE_ALL & ~SSD_STAGE_STATE) : (uint32_t)SSD_STAGE_ALL;
+    if (joint) {
+        const int c = fwd_impl(SSD_STAGE_STATE, dims, tuning, layout, x, d_raw, d_init, B, C, init_fwd,
+                               nullptr, 0, y_fwd, final_fwd, wf, half, stream, wr);
+        if (c != SSD_OK) return c;
+    }
+    for (int r = 0; r < 2; ++r) {
+        const int c = ssd_fwd_ex(rest, dims, tuning, layout, x, d_raw, d_init, B, C,
+                                 r ? init_rev : init_fwd, nullptr, r, r ? y_rev : y_fwd,
+                                 r ? final_rev : final_fwd, r ? wr : wf, half, stream);
+        if (c != SSD_OK) return c;
     }
     return SSD_OK;
 }

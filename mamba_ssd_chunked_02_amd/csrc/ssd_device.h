@@ -287,8 +287,17 @@ struct __attribute__((aligned(16))) DecayS {
     float cs2[kChunk];
     float w[kChunk];
 };
+// Both directions' chunk-state factors (the pass forming the forward and the
+// reverse span states in one walk): the forward weights as in DecayS, and
+// wr = 2^{cs_{s-1}} d_s, the decay of the chunk's tokens before s times d_s.
+struct __attribute__((aligned(16))) DecayS2 {
+    float cs2[kChunk];
+    float w[kChunk];
+    float wr[kChunk];
+};
 __device__ __forceinline__ float chunk_decay(const Decay& D) { return D.fe[kChunk - 1]; }
 __device__ __forceinline__ float chunk_decay(const DecayS& D) { return fexp2(D.cs2[kChunk - 1]); }
+__device__ __forceinline__ float chunk_decay(const DecayS2& D) { return fexp2(D.cs2[kChunk - 1]); }
 
 // Span states are kept in MFMA result order so each wave moves 64 contiguous
 // 4-value groups: within one (span, head) block of P*N values, state entry
@@ -332,6 +341,16 @@ __device__ __forceinline__ void decay_factors(DecayS& D, uint32_t raw, float d_i
     const float v = wave_prefix_sum(-dt * kLog2e);
     D.cs2[lane] = v;
     D.w[lane] = grad ? (lane < clen ? fexp2(v) : 0.f) : fexp2(lane_value(v, 63) - v) * dt;
+}
+template <typename T>
+__device__ __forceinline__ void decay_factors(DecayS2& D, uint32_t raw, float d_init, int clen,
+                                              int lane, bool) {
+    const float draw = __uint_as_float(sizeof(T) == 2 ? raw << 16 : raw);
+    const float dt = lane < clen ? softplus(draw + d_init) : 0.f;
+    const float v = wave_prefix_sum(-dt * kLog2e);
+    D.cs2[lane] = v;
+    D.w[lane] = fexp2(lane_value(v, 63) - v) * dt;
+    D.wr[lane] = fexp2(v + dt * kLog2e) * dt;  // v + dt log2e: the sum over tokens before s
 }
 
 }  // namespace

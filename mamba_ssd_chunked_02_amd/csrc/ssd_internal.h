@@ -78,6 +78,8 @@ struct KParams {
                             // flows against the processing order)
     void* span_states;      // (chunk_run) [nspan][H][P][N], input type
     float* span_decay;      // (chunk_run) [nspan][H]
+    void* rev_states;       // (both directions) the reverse pass's span states
+    float* rev_decay;       // ... and span decays, same layout as states / decay
     int32_t state_f32;      // span states stored in float32 whatever the input
                             // type (span kernels, plans 0 and 1)
     float d_init;
@@ -153,6 +155,7 @@ hipError_t launch_span_table(const int32_t* cu_raw, int32_t nseq, int64_t T,
                              int32_t K, int64_t nspan, int32_t* cu_san,
                              int32_t* span_off, int4* table, hipStream_t s);
 hipError_t launch_span_state(const KParams& p, int dtype, int N, hipStream_t s);
+hipError_t launch_span_state_both(const KParams& p, int dtype, int N, hipStream_t s);
 hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s);
 hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s);
 // The backward pass's two chunk-state passes (pa: kModeState on (B, x), pb:

@@ -80,7 +80,7 @@ __device__ __forceinline__ const V& dep_on(Tag, const V& v) { return v; }
 // has one buffer, refilled as soon as the step's C reads are done.  Decay
 // factors are formed four chunks at a time (one chunk per wave of a quad)
 // from d_raw loaded one such batch ahead.
-template <typename T, int N, int HG, bool SCAN>
+template <typename T, int N, int HG, bool SCAN, bool BOTH = false>
 struct __attribute__((aligned(16))) Smem {
     using X4 = typename Vec<T>::x4;
     T xs[2][HG][kChunk * kPGroup];      // X of every head, this group's 64 columns
@@ -92,7 +92,7 @@ struct __attribute__((aligned(16))) Smem {
     X4 lf[SCAN ? HG : 1][SCAN ? 6 : 1][2][SCAN ? 64 : 1];
     // chunk 4b + w of the current batch b, per head (a state pass keeps only
     // what its update needs)
-    std::conditional_t<SCAN, Decay, DecayS> dec[kWaves][HG];
+    std::conditional_t<SCAN, Decay, std::conditional_t<BOTH, DecayS2, DecayS>> dec[kWaves][HG];
     __attribute__((aligned(16))) uint32_t dr[2][kWaves][HG][kChunk];  // d_raw of a batch, per lane
     uint32_t ticket, epoch;  // fused kernel: this workgroup's ticket and epoch
 };
@@ -138,8 +138,10 @@ __device__ __forceinline__ void mask_tile(Smem<T, N, HG, SCAN>& sm, const Decay&
 // workgroup needs two waves per SIMD to fit a CU at all).  The variants whose
 // fragments and state need more (bf16 d_state 256; fp32 d_state 128 states,
 // fp32 d_state >= 64 scans) get one wave per SIMD and up to 512 VGPRs.
-enum { kModeState = 0, kModeScan = 1, kModeFused = 2, kModeStateGrad = 3 };
-constexpr bool is_state(int mode) { return mode == kModeState || mode == kModeStateGrad; }
+enum { kModeState = 0, kModeScan = 1, kModeFused = 2, kModeStateGrad = 3, kModeStateBoth = 4 };
+constexpr bool is_state(int mode) {
+    return mode == kModeState || mode == kModeStateGrad || mode == kModeStateBoth;
+}
 template <typename T, int N, int HG, int MODE>
 constexpr int span_occupancy() {
     if (HG != 1) return 2;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" :
 //              local state (no later span reads it) and writes final_state.
 template <typename T, int N, int HG, int MODE>
 __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
-                                          Smem<T, N, HG, !is_state(MODE)>& sm) {
+                                          Smem<T, N, HG, !is_state(MODE), MODE == kModeStateBoth>& sm) {
     using Cf = Cfg<T, N, HG>;
     using X8 = typename Vec<T>::x8;
     using X4 = typename Vec<T>::x4;
@@ -413,6 +415,14 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) Hs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float logdec2 = 0.f;  // first wave of each quad: sum of its chunk log2-decays
+    // (both directions) the reverse local state of the span, gathered as the
+    // span is walked forwards: every token's input weighted by the decay of
+    // the span's tokens before it; lb = log2 decay of the chunks walked
+    constexpr int NBR = MODE == kModeStateBoth ? NB : 1;
+    f32x4 Hr[NBR];
+#pragma unroll
+    for (int nb = 0; nb < NBR; ++nb) Hr[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lb = 0.f;
     auto state_ptr = [&](int64_t sp) -> T* {
         return (T*)p.states + (sp * p.H + h) * (int64_t)p.P * N;
     };
@@ -492,13 +502,13 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         constexpr bool SCAN = decltype(scan_tag)::value;
         // a chunk's decay factors, and the state update weights among them
         auto form_dec = [&](auto& D, uint32_t raw, int cl) {
-            if constexpr (std::is_same_v<std::decay_t<decltype(D)>, DecayS>)
+            if constexpr (!std::is_same_v<std::decay_t<decltype(D)>, Decay>)
                 decay_factors<T>(D, raw, p.d_init, cl, lane, MODE == kModeStateGrad);
             else
                 decay_factors<T>(D, raw, p.d_init, cl, lane);
         };
         auto state_w = [&](const auto& D, int s0) -> const float* {
-            if constexpr (std::is_same_v<std::decay_t<decltype(D)>, DecayS>) return &D.w[s0];
+            if constexpr (!std::is_same_v<std::decay_t<decltype(D)>, Decay>) return &D.w[s0];
             else return MODE == kModeStateGrad ? &D.fe[s0] : &D.w[s0];
         };
         if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
@@ -678,9 +688,18 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                         for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * ws[j]);
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) Hs[nb] = mma(bt[nb], b, Hs[nb]);
+                        if constexpr (MODE == kModeStateBoth) {
+                            const float pre = fexp2(lb);  // the chunks before this one
+                            const f32x8 wr = ld8(&D.wr[s0]);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) b[j] = cvt<T>((float)xv[j] * (wr[j] * pre));
+#pragma unroll
+                            for (int nb = 0; nb < NB; ++nb) Hr[nb] = mma(bt[nb], b, Hr[nb]);
+                        }
                     }
                 }
                 if (!SCAN && w4 == 0) logdec2 += D.cs2[kChunk - 1];
+                if (MODE == kModeStateBoth) lb += D.cs2[kChunk - 1];
                 if (!SCAN && chunk_out && !p.chunk_run) {
                     // this chunk's local state; the next starts from zero
                     if (active) {
@@ -731,6 +750,23 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
             }
         }
         if (pg == 0 && w4 == 0 && live && lane == 0) p.decay[span * p.H + h] = fexp2(logdec2);
+        if constexpr (MODE == kModeStateBoth) {
+            // the reverse pass's span kin' = sps - 1 - kin of the sequence
+            // covers the same tokens (whole spans: L a multiple of 64 K)
+            const int64_t rspan = span + (p.sps - 1 - 2 * (int64_t)kin);
+            if (active) {
+                if (p.state_f32) {
+                    float* const rp = (float*)p.rev_states + (rspan * p.H + h) * (int64_t)p.P * N;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) store4(rp + state_off(pb, nb, lane, NB), Hr[nb]);
+                } else {
+                    T* const rp = (T*)p.rev_states + (rspan * p.H + h) * (int64_t)p.P * N;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) store4(rp + state_off(pb, nb, lane, NB), Hr[nb]);
+                }
+            }
+            if (pg == 0 && w4 == 0 && live && lane == 0) p.rev_decay[rspan * p.H + h] = fexp2(logdec2);
+        }
         return;
     }
 
@@ -821,7 +857,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 template <typename T, int N, int HG, int MODE>
 __global__ __launch_bounds__(kThreads * HG, (span_occupancy<T, N, HG, MODE>())) void span_kernel(
     KParams p) {
-    __shared__ Smem<T, N, HG, !is_state(MODE)> sm;
+    __shared__ Smem<T, N, HG, !is_state(MODE), MODE == kModeStateBoth> sm;
     touch_args(p);
     span_body<T, N, HG, MODE>(p, blockIdx.x, sm);
 }
@@ -1136,6 +1172,27 @@ hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s) {
                             : launch_span<kModeScan>(p, dtype, N, s);
 }
 
+// Both directions' span states in one walk (one head per workgroup; batch
+// mode, whole spans).
+hipError_t launch_span_state_both(const KParams& p, int dtype, int N, hipStream_t s) {
+    if (p.hg_state != 1 || p.nseq) return hipErrorInvalidValue;
+    if (dtype == 1) {
+        switch (N) {
+            case 16: return launch_span_hg<bf16, 16, 1, kModeStateBoth>(p, 1, s);
+            case 32: return launch_span_hg<bf16, 32, 1, kModeStateBoth>(p, 1, s);
+            case 64: return launch_span_hg<bf16, 64, 1, kModeStateBoth>(p, 1, s);
+            case 128: return launch_span_hg<bf16, 128, 1, kModeStateBoth>(p, 1, s);
+        }
+    } else {
+        switch (N) {
+            case 16: return launch_span_hg<float, 16, 1, kModeStateBoth>(p, 1, s);
+            case 32: return launch_span_hg<float, 32, 1, kModeStateBoth>(p, 1, s);
+            case 64: return launch_span_hg<float, 64, 1, kModeStateBoth>(p, 1, s);
+            case 128: return launch_span_hg<float, 128, 1, kModeStateBoth>(p, 1, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
 hipError_t launch_span_state_pair(const KParams& pa, const KParams& pb, int dtype, int N,
                                   hipStream_t s) {
     const int64_t n = pa.nspan * pa.H * pa.npg;  // one head per workgroup (both halves)

@@ -389,6 +389,60 @@ def test_bidir_matches_two_calls(ssd):
     assert O.rel_err(yr.float().cpu(), yo) <= 1e-2
 
 
+# (batch, seqlen, nheads, headdim, d_state, dtype, tuning): whole spans, so
+# one launch forms both directions' span states
+BIDIR_JOINT = [
+    (2, 512, 3, 64, 64, "bf16", None),  # the planner's one-chunk spans, folded in the scan
+    (1, 1024, 2, 192, 64, "bf16", {"kernel": "hw", "chunks_per_span": 4}),  # head-wave scan, 3 column groups
+    (2, 768, 2, 64, 128, "bf16", {"kernel": "span", "chunks_per_span": 3, "state_pass": "pass"}),
+    (1, 256, 2, 32, 16, "f32", None),
+    (1, 512, 2, 64, 32, "f32", {"kernel": "span", "chunks_per_span": 8, "state_pass": "fold"}),
+    (3, 384, 2, 16, 32, "bf16", {"kernel": "span", "chunks_per_span": 2, "state_pass": "pass"}),
+]
+
+
+@pytest.mark.parametrize("case", BIDIR_JOINT, ids=lambda c: "x".join(map(str, c[:6])) + ("-" + "-".join(
+    f"{k}{v}" for k, v in c[6].items()) if c[6] else ""))
+def test_bidir_joint_span_states(ssd, case):
+    """ssd_fwd_bidir where every span is whole: the forward and the reverse
+    span states come from one walk over each span.  Each direction against
+    the oracle from its own initial state (y and final state), and against
+    the one-direction calls within the same bound."""
+    b, L, H, P, N, dt, tun = case
+    p = random_problem(173, b, L, H, P, N, dtype=dt, init_scale=0.5, d_init=-3.0)
+    g = torch.Generator().manual_seed(5)
+    init_rev = 0.5 * torch.randn(p["init_state"].shape, generator=g)
+    q = dict(p, init_state=init_rev)
+    dims = ssd.dims_for(p["x"], p["B"])
+    plan = ssd.ssd_fwd_plan(dims, tun)
+    assert L % (64 * plan.chunks_per_span) == 0 and plan.fused_pass != 2
+    d = to_dev(p)
+    call = ssd.prepare_bidir(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                             init_fwd=d["init_state"], init_rev=init_rev.to(DEV),
+                             final_state=True, tuning=tun)
+    y, (ff, fr) = call.run()
+    torch.cuda.synchronize()
+    tol = TOL[p["x"].dtype]
+    yf_ref, ff_ref = oracle(p, False)
+    yr_ref, fr_ref = oracle(q, True)
+    errs = {"y_fwd": O.rel_err(y[..., :P].float().cpu(), yf_ref),
+            "y_rev": O.rel_err(y[..., P:].float().cpu(), yr_ref),
+            "final_fwd": O.rel_err(ff.cpu(), ff_ref), "final_rev": O.rel_err(fr.cpu(), fr_ref)}
+    yf1, ff1 = run(ssd, p, False, tuning=tun)
+    yr1, fr1 = run(ssd, q, True, tuning=tun)
+    errs["vs_calls_rev"] = O.rel_err(y[..., P:].float().cpu(), yr1.double())
+    errs["vs_calls_final_rev"] = O.rel_err(fr.cpu(), fr1.double())
+    print("bidir joint", case, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert torch.isfinite(y.float()).all()
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    errs_f = (O.rel_err(y[..., :P].float().cpu(), yf1.double()), O.rel_err(ff.cpu(), ff1.double()))
+    assert max(errs_f) <= tol, errs_f
+    if not plan.head_wave:
+        # the span kernels' forward state is the one-direction call's arithmetic
+        assert torch.equal(y[..., :P].float().cpu(), yf1) and torch.equal(ff.cpu(), ff1)
+
+
 # ------------------------------------------------------------ boundary
 def test_ssd_check_rejects_bad_cu_seqlens(ssd, monkeypatch):
     """With SSD_CHECK=1 the library copies cu_seqlens to the host and
