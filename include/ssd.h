@@ -260,7 +260,8 @@ int ssd_fwd_ex(uint32_t stage_mask, const ssd_dims* dims, const ssd_tuning* tuni
 /*
  * Both directions of the bidirectional mode (jsqmd.com page §3.1: the
  * causal scan and the same scan over the time-flipped sequence, their
- * outputs concatenated) in one call, batch mode only (no cu_seqlens):
+ * outputs concatenated) in one call, batch mode only (nseq > 0 returns
+ * SSD_ERR_SHAPE):
  * y_fwd, final_fwd are ssd_fwd's outputs with reverse = 0 from init_fwd,
  * y_rev, final_rev those with reverse = 1 from init_rev.  Both outputs
  * follow layout's y strides (for example the two halves of one

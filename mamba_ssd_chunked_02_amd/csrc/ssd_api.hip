@@ -622,6 +622,7 @@ int ssd_fwd_bidir(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layo
     Plan pl;
     const int st = make_plan(dims, tuning, &pl);
     if (st != SSD_OK) return st;
+    if (dims->nseq > 0) return SSD_ERR_SHAPE;  // batch mode only
     const size_t half = align_up(pl.total);
     if (half > 0 && (!workspace || workspace_bytes < 2 * half)) return SSD_ERR_WORKSPACE;
     char* const wf = (char*)workspace;

@@ -128,6 +128,46 @@ def test_rejects_bad_arguments(m):
     assert call(m, ok, ws=FAKE + 16) == -4
 
 
+def test_bidir_workspace_bytes(m):
+    """Two forward workspaces, each rounded up to 256 bytes; 0 for sizes
+    ssd_fwd rejects."""
+    from ssd_inputs import WORKLOADS
+    for w in WORKLOADS.values():
+        d = m.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.d_state, w.ngroups,
+                        w.chunk_size, w.nseq, m.SSD_BF16 if w.dtype == "bf16" else m.SSD_F32)
+        one = m.ssd_fwd_workspace_bytes(d)
+        assert m.library().ssd_fwd_bidir_workspace_bytes(ctypes.byref(d)) == 2 * ((one + 255) // 256 * 256)
+    bad = m.make_dims(1, 64, 2, 24, 16)
+    assert m.library().ssd_fwd_bidir_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def call_bidir(m, dims, **kw):
+    args = dict(x=FAKE, d_raw=FAKE, B=FAKE, C=FAKE, init_f=None, init_r=None, y_f=FAKE,
+                y_r=FAKE + 4096, fin_f=None, fin_r=None, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    vp = lambda v: None if v is None else ctypes.c_void_p(v)
+    a = args
+    return m.library().ssd_fwd_bidir(
+        ctypes.byref(dims), None, None, vp(a["x"]), vp(a["d_raw"]), -4.6, vp(a["B"]), vp(a["C"]),
+        vp(a["init_f"]), vp(a["init_r"]), vp(a["y_f"]), vp(a["y_r"]), vp(a["fin_f"]),
+        vp(a["fin_r"]), vp(a["ws"]), a["wsb"], None)
+
+
+@needs_no_gpu
+def test_bidir_rejects_bad_arguments(m):
+    """Either direction's bad argument is reported before anything is queued
+    (a launch with these made-up pointers would fail with SSD_ERR_HIP)."""
+    ok = m.make_dims(1, 1024, 2, 64, 128)
+    half = (m.ssd_fwd_workspace_bytes(ok) + 255) // 256 * 256
+    assert call_bidir(m, ok, x=None) == -1
+    assert call_bidir(m, ok, y_r=None) == -1
+    assert call_bidir(m, ok, y_r=FAKE + 2) == -4
+    assert call_bidir(m, ok, ws=None) == -6
+    assert call_bidir(m, ok, wsb=half) == -6                        # one direction's worth
+    assert call_bidir(m, ok, init_r=FAKE, fin_r=FAKE + 64) == -9    # OVERLAP
+    assert call_bidir(m, m.make_dims(1, 1024, 2, 64, 128, nseq=2)) == -2  # batch mode only
+
+
 @needs_no_gpu
 def test_rejects_bad_strides(m):
     """Rows of x, B, C and y are 16-byte units; every stride is >= 0 and
