@@ -511,10 +511,12 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
             if constexpr (!std::is_same_v<std::decay_t<decltype(D)>, Decay>) return &D.w[s0];
             else return MODE == kModeStateGrad ? &D.fe[s0] : &D.w[s0];
         };
-        if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
-        if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
-        issue_xb(0, sm.xs[0][q], sm.bs[0]);
-        if (SCAN) issue_c(0, sm.cs);
+        if constexpr (MODE != kModeScan) {  // (span_scan issued these before its entering state)
+            if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
+            if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
+            issue_xb(0, sm.xs[0][q], sm.bs[0]);
+            if (SCAN) issue_c(0, sm.cs);
+        }
         if (MODE == kModeFused && SCAN) {
             // the fused kernel's fold loads go out with the first tiles
 #pragma unroll
@@ -809,6 +811,12 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     }
 
     if constexpr (MODE == kModeScan) {
+        // The first chunk's tiles and d_raw go out first: their loads into
+        // LDS overlap the forming of the entering state below.
+        if (w4 < nck) issue_d(w4, sm.dr[0][w4][q]);
+        if (kWaves + w4 < nck) issue_d(kWaves + w4, sm.dr[1][w4][q]);
+        issue_xb(0, sm.xs[0][q], sm.bs[0]);
+        issue_c(0, sm.cs);
         // (span_scan) the state entering the span: as state_pass left it in
         // place of the span state, or folded here span by span
         if (active) {
