@@ -374,6 +374,11 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     u32x4 rgs[SI], rhs[SI];
     float dgs = 0.f, dhs = 0.f;
     const bool carried = p.hspan != nullptr;
+    // (carried) the chunk-state walks start each span from zero: the state
+    // entering the span's first chunk and the gradient leaving its last one
+    // are the span's whole parts, whose within-span slots are not written
+    const bool h_first = carried && kc % 4 == 0;
+    const bool g_first = carried && (kc % 4 == 3 || kc == (len + kChunk - 1) / kChunk - 1);
     // the chunk's four-chunk span
     const int64_t span4 = !carried ? 0
                           : p.nseq ? (int64_t)p.span_off4[p.table[chunk].x] + kc / 4
@@ -404,8 +409,9 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         for (int k = 0; k < SI; ++k) {
             const int o = ((wave + kBWaves * k) * 64 + lane) * EPU;
             if (o < PN) {
-                rg[k] = *(const u32x4*)((const T*)p.gout + hb + o);
-                rh[k] = *(const u32x4*)((const T*)p.hprev + hb + o);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                rg[k] = g_first ? z : *(const u32x4*)((const T*)p.gout + hb + o);
+                rh[k] = h_first ? z : *(const u32x4*)((const T*)p.hprev + hb + o);
             }
         }
         if (carried) {

@@ -550,9 +550,10 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
             // After chunk c's loads this wave issued, in an active scan wave,
             // exactly four y stores (the previous chunk is full), else nothing.
             // (chunk_out) after chunk c's loads, an active state wave stored
-            // exactly NB entries of the previous chunk's state.
+            // exactly NB entries of the previous chunk's state (a carried
+            // walk stores none at its first chunk).
             if (SCAN && active && c > 0) vm_wait<4>();
-            else if (!SCAN && chunk_out && active && c > 0) vm_wait<NB>();
+            else if (!SCAN && chunk_out && active && c > 0 && (c > 1 || !p.chunk_run)) vm_wait<NB>();
             else vm_wait<0>();
             block_sync();  // every wave's loads of chunk c are in LDS
             if (c > 0 && c % kWaves == 0) {
@@ -568,9 +569,10 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
                             const T* __restrict__ ct, T* __restrict__ xn, T* __restrict__ bn,
                             T* __restrict__ cn) {
                 if (!last) issue_xb(c + 1, xn, bn);
-                if (!SCAN && chunk_out && p.chunk_run && active) {
+                if (!SCAN && chunk_out && p.chunk_run && active && c > 0) {
                     // (carried chunk states) the span-local state entering
-                    // this chunk: the chunks walked before it
+                    // this chunk: the chunks walked before it (none before
+                    // the first: its slot is not written, and not read)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
                         store4_async(state_ptr(slot0 + ck(c)) + state_off(pb, nb, lane, NB), Hs[nb]);
