@@ -398,6 +398,7 @@ BIDIR_JOINT = [
     (1, 256, 2, 32, 16, "f32", None),
     (1, 512, 2, 64, 32, "f32", {"kernel": "span", "chunks_per_span": 8, "state_pass": "fold"}),
     (3, 384, 2, 16, 32, "bf16", {"kernel": "span", "chunks_per_span": 2, "state_pass": "pass"}),
+    (2, 512, 2, 64, 128, "bf16", {"kernel": "span", "chunks_per_span": 4, "state_f32": 1}),  # fp32 span states
 ]
 
 
@@ -441,6 +442,29 @@ def test_bidir_joint_span_states(ssd, case):
     if not plan.head_wave:
         # the span kernels' forward state is the one-direction call's arithmetic
         assert torch.equal(y[..., :P].float().cpu(), yf1) and torch.equal(ff.cpu(), ff1)
+
+
+def test_bidir_joint_in_place_final_states(ssd):
+    """ssd_fwd_bidir with each direction's final state written over its
+    initial state (whole spans, so the joint state launch runs; the aliased
+    directions then pass their states in the separate pass)."""
+    p = random_problem(181, 2, 512, 2, 64, 64, dtype="bf16", init_scale=0.5, d_init=-3.0)
+    g = torch.Generator().manual_seed(7)
+    init_rev = 0.5 * torch.randn(p["init_state"].shape, generator=g)
+    d = to_dev(p)
+    sf = d["init_state"].clone()
+    sr = init_rev.to(DEV)
+    call = ssd.prepare_bidir(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_fwd=sf,
+                             init_rev=sr, final_state=(sf, sr))
+    y, _ = call.run()
+    torch.cuda.synchronize()
+    P = p["x"].shape[3]
+    yf_ref, ff_ref = oracle(p, False)
+    yr_ref, fr_ref = oracle(dict(p, init_state=init_rev), True)
+    errs = [O.rel_err(y[..., :P].float().cpu(), yf_ref), O.rel_err(y[..., P:].float().cpu(), yr_ref),
+            O.rel_err(sf.cpu(), ff_ref), O.rel_err(sr.cpu(), fr_ref)]
+    print("bidir in place", ["%.2e" % e for e in errs], flush=True)
+    assert max(errs) <= TOL[torch.bfloat16], errs
 
 
 # ------------------------------------------------------------ boundary
