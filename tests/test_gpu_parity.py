@@ -444,6 +444,38 @@ def test_bidir_joint_span_states(ssd, case):
         assert torch.equal(y[..., :P].float().cpu(), yf1) and torch.equal(ff.cpu(), ff1)
 
 
+@pytest.mark.parametrize("dtype,cuts", [("bf16", [0, 256, 640, 1024]), ("bf16", [0, 100, 577, 1024]),
+                                         ("f32", [0, 64, 65, 300, 1024])])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_sequence_shards_chained(ssd, dtype, cuts, reverse):
+    """The one-GPU rehearsal of sequence sharding: each shard of a sequence
+    is its own call, started from the state the previous shard left (the
+    shards walked in processing order), and the shards' outputs and the last
+    final state equal one call over the whole sequence and the oracle."""
+    p = random_problem(191, 2, cuts[-1], 3, 32, 64, dtype=dtype, init_scale=0.5, d_init=-3.0)
+    d = to_dev(p)
+    tol = TOL[p["x"].dtype]
+    y_all, f_all = ssd.ssd_fwd(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"],
+                               init_state=d["init_state"], reverse=reverse)
+    shards = list(zip(cuts[:-1], cuts[1:]))
+    if reverse:
+        shards = shards[::-1]
+    y = torch.empty_like(y_all)
+    state = d["init_state"]
+    for lo, hi in shards:
+        sl = lambda t: t[:, lo:hi].contiguous()
+        ys, state = ssd.ssd_fwd(sl(d["x"]), sl(d["d_raw"]), d["d_init"], sl(d["B"]), sl(d["C"]),
+                                init_state=state, reverse=reverse)
+        y[:, lo:hi] = ys
+    torch.cuda.synchronize()
+    yr, fr = oracle(p, reverse)
+    errs = [O.rel_err(y.float().cpu(), yr), O.rel_err(state.cpu(), fr),
+            O.rel_err(y.float().cpu(), y_all.float().cpu().double()),
+            O.rel_err(state.cpu(), f_all.cpu().double())]
+    print("shards", dtype, cuts, reverse, ["%.2e" % e for e in errs], flush=True)
+    assert max(errs) <= tol, errs
+
+
 def test_bidir_joint_in_place_final_states(ssd):
     """ssd_fwd_bidir with each direction's final state written over its
     initial state (whole spans, so the joint state launch runs; the aliased
