@@ -283,9 +283,12 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         const int64_t per = n / kXcds, rem = n % kXcds;
         return x * per + (x < rem ? x : rem) + b / kXcds;
     }();
-    const int sub = (int)(item % p.nsub);
-    const int grp = (int)((item / p.nsub) % p.G);
-    const int64_t chunk = item / p.nsub / p.G;
+    // (divisions as multiply-highs set on the host: items stay below 2^31)
+    const uint32_t it32 = (uint32_t)item, isub = fdiv(it32, p.by_nsub);
+    const int sub = (int)(it32 - isub * (uint32_t)p.nsub);
+    const uint32_t chunk32 = fdiv(isub, p.by_G);
+    const int grp = (int)(isub - chunk32 * (uint32_t)p.G);
+    const int64_t chunk = chunk32;
     int64_t start = 0, len = 0, kc = 0;
     bool valid = true;
     if (p.nseq) {
@@ -298,8 +301,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
             kc = e.y;
         }
     } else {
-        const int64_t seq = chunk / p.cps;
-        kc = chunk - seq * p.cps;
+        const uint32_t seq = fdiv(chunk32, p.by_cps);
+        kc = (int64_t)(chunk32 - seq * (uint32_t)p.cps);
         start = seq * p.L;
         len = p.L;
     }
@@ -325,7 +328,10 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     // before one store per head.
     const int P = p.P, npg = (P + kPGroup - 1) / kPGroup;
     const int nunit = (h1 - h0) * npg;
-    auto ucols = [&](int u) { return min(kPGroup, P - kPGroup * (u % npg)); };
+    // unit u: head u / npg, column group u % npg
+    auto uhead = [&](int u) { return (int)fdiv((uint32_t)u, p.by_npg); };
+    auto ugrp = [&](int u) { return u - uhead(u) * npg; };
+    auto ucols = [&](int u) { return min(kPGroup, P - kPGroup * ugrp(u)); };
     // token strides (the host keeps them <= 2^24)
     const int BS = (int)p.bs_t, CS = (int)p.cs_t;
     issue_tile<(BI + kBWaves - 1) / kBWaves, kBWaves, BI>(sm.bs, (const T*)p.B + tb0 * BS + grp * p.bs_g,
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         return clen == kChunk || r < clen ? r * rstride + col : col;
     };
     auto fetch = [&](int u) {
-        const int h = h0 + u / npg, pcol0 = kPGroup * (u % npg);
+        const int h = h0 + uhead(u), pcol0 = kPGroup * ugrp(u);
         const int npb = ucols(u) / 16, PN = ucols(u) * N;
         const T* xr = (const T*)p.x + tb0 * p.xs_t + h * p.xs_h + pcol0;
         const T* gr = (const T*)p.dy + tb0 * p.gs_t + h * p.gs_h + pcol0;
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     // per-token sums of unit u -> its part of d d_raw (wave 0, lane = token):
     // da from its four terms (T1 + T2 + T3 + T4 above)
     auto tail = [&](int u) {
-        const int h = h0 + u / npg;
+        const int h = h0 + uhead(u);
         const BDecay& D = sm.dec[u % 3];
         const int par = u & 1;
         store_dd();
@@ -528,8 +534,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
         const float p4 = wave_prefix_sum(v4) - v4;                // T4: k < s
         const float da = D.fe[kChunk - 1] * ghs + p2 + s3 + p4;
         const float gr = (dw - da) * D.sg[s];
-        dd_acc = u % npg == 0 ? gr : dd_acc + gr;
-        if (u % npg == npg - 1) {
+        dd_acc = ugrp(u) == 0 ? gr : dd_acc + gr;
+        if (ugrp(u) == npg - 1) {
             dd_val = dd_acc;
             dd_at = in ? tok(s) * p.ds_t + (int64_t)h * p.ds_h : -1;
         }
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
     };
 
     for (int u = 0; u < nunit; ++u) {
-        const int h = h0 + u / npg, pcol0 = kPGroup * (u % npg), npb = ucols(u) / 16;
+        const int h = h0 + uhead(u), pcol0 = kPGroup * ugrp(u), npb = ucols(u) / 16;
         const BDecay& D = sm.dec[u % 3];
         stash(u);
         block_sync();
@@ -594,7 +600,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_chunk_kernel(BParams p) {
             }
         }
         if (wave == kFW && u + 1 < nunit)
-            bwd_factors<T>(sm.dec[(u + 1) % 3], sm.dr[(u + 1) / npg][lane], p.d_init, clen, lane);
+            bwd_factors<T>(sm.dec[(u + 1) % 3], sm.dr[uhead(u + 1)][lane], p.d_init, clen, lane);
         block_sync();
 
         // dX for headdim block w4, token blocks 2q and 2q + 1 (transposed:
@@ -798,8 +804,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* pb, const 
 template <typename T, int N>
 hipError_t launch_bwd_t(const BParams& p, hipStream_t s) {
     const int64_t grid = p.nchunk * p.G * p.nsub;
+    if (grid >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    BParams q = p;
+    q.by_nsub = make_fastdiv((uint32_t)p.nsub);
+    q.by_G = make_fastdiv((uint32_t)p.G);
+    q.by_cps = make_fastdiv((uint32_t)p.cps);
+    q.by_npg = make_fastdiv((uint32_t)((p.P + kPGroup - 1) / kPGroup));
     if (grid > 0)
-        hipLaunchKernelGGL((bwd_chunk_kernel<T, N>), dim3((unsigned)grid), dim3(kBThreads), 0, s, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<T, N>), dim3((unsigned)grid), dim3(kBThreads), 0, s, q);
     return hipGetLastError();
 }
 

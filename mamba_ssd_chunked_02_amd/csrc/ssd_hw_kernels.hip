@@ -238,15 +238,18 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
     // head groups, which share B and C) land on the same XCD and its L2.
-    const int ngrp = p.H / HG;
-    const int64_t nreal = p.nspan * ngrp * p.npg;
-    const int64_t per = (nreal + kXcds - 1) / kXcds;
+    // (divisions by the launch's sizes as multiply-highs, set on the host;
+    // work items stay below 2^31)
+    const Decode& dc = p.dc;
+    const int ngrp = dc.ngrp;  // H / HG
     const int64_t bid = blockIdx.x;
-    const int64_t logical = (bid % kXcds) * per + bid / kXcds;
-    if (logical >= nreal) return;
-    const int pg = (int)(logical % p.npg);
-    const int hgi = (int)((logical / p.npg) % ngrp);
-    const int64_t span = logical / ((int64_t)p.npg * ngrp);
+    const int64_t logical = (bid % kXcds) * dc.per + bid / kXcds;
+    if (logical >= dc.nreal) return;
+    const uint32_t lg32 = (uint32_t)logical, rest = fdiv(lg32, dc.by_npg);
+    const int pg = (int)(lg32 - rest * (uint32_t)p.npg);
+    const uint32_t span32 = fdiv(rest, dc.by_ngrp);
+    const int hgi = (int)(rest - span32 * (uint32_t)ngrp);
+    const int64_t span = span32;
     const int h0 = hgi * HG;
 
     int64_t start, len;
@@ -259,9 +262,9 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE
         chunk0 = e.y;
         nck = e.z;
     } else {
-        const int64_t seq = span / p.sps;
-        const int kin = (int)(span - seq * p.sps);
-        start = seq * p.L;
+        const uint32_t seq = fdiv(span32, dc.by_sps);
+        const int kin = (int)(span32 - seq * (uint32_t)p.sps);
+        start = (int64_t)seq * p.L;
         len = p.L;
         const int64_t nch = (len + kChunk - 1) / kChunk;
         chunk0 = kin * p.K;
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE
     const int dir = p.reverse ? -1 : 1;
     // token strides (the host keeps them <= 2^24)
     const int XS = (int)p.xs_t, BS = (int)p.bs_t, CS = (int)p.cs_t, DS = (int)p.ds_t;
-    const int grp = (int)((int64_t)h0 * p.G / p.H);
+    const int grp = (int)fdiv((uint32_t)h0, dc.by_hpg);  // h0 G / H
     const bf16* const xg = (const bf16*)p.x + (int64_t)h * p.xs_h + pcol0;
     const bf16* const bg = (const bf16*)p.B + (int64_t)grp * p.bs_g;
     const bf16* const cg = (const bf16*)p.C + (int64_t)grp * p.cs_g;
@@ -590,8 +593,10 @@ hipError_t launch_hw_t(const KParams& p, hipStream_t s) {
     const int64_t nreal = p.nspan * (p.H / HG) * p.npg;
     if (nreal == 0) return hipSuccess;
     const int64_t grid = (nreal + kXcds - 1) / kXcds * kXcds;
+    KParams q = p;
+    set_decode(q, HG);
     hipLaunchKernelGGL((hw_span_kernel<N, HG, NPB, MODE>), dim3((unsigned)grid),
-                       dim3(HwCfg<N, HG, NPB>::TH), 0, s, p);
+                       dim3(HwCfg<N, HG, NPB>::TH), 0, s, q);
     return hipGetLastError();
 }
 

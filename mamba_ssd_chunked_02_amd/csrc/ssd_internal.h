@@ -15,6 +15,37 @@ constexpr int kPGroup = 64;    // headdim columns per workgroup (16 per wave)
 constexpr int kXcds = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kXcdCus = 32;    // MI355X: 32 CUs per XCD
 
+// n / d for 0 <= n < 2^31 as a multiply-high, an add and a shift: with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, the quotient is
+// (mulhi(n, m) + n) >> l (Granlund and Montgomery, "Division by Invariant
+// Integers using Multiplication", PLDI 1994, section 4; for such n the sum
+// stays below 2^32).  A launch's divisors are fixed, so its launcher picks m
+// and l on the host and the kernels' index decode needs no division.
+struct FastDiv {
+    uint32_t m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f{1u, 0u};  // d <= 1: n itself
+    if (d <= 1) return f;
+    while ((1ull << f.l) < d) ++f.l;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << f.l) - d)) / d + 1);
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+// A span launch's grid decode, filled in by its launcher (set_decode) from
+// the sizes below and the launch's heads per workgroup.
+struct Decode {
+    int64_t nreal;   // work items: span slots x head groups x column groups
+    int64_t per;     // work items per XCD, ceil(nreal / kXcds)
+    int32_t ngrp;    // head groups of the launch's heads per workgroup
+    int32_t nchain;  // chains: batch x ngrp x npg
+    int32_t cpx;     // chains per XCD, nchain / kXcds
+    FastDiv by_npg, by_ngrp, by_cpx, by_sps, by_batch, by_hpg;  // hpg = H / G
+};
+
 // Everything the kernels need, passed by value.
 struct KParams {
     const void* x;          // [b, L, H, P]
@@ -83,7 +114,25 @@ struct KParams {
     int32_t state_f32;      // span states stored in float32 whatever the input
                             // type (span kernels, plans 0 and 1)
     float d_init;
+    Decode dc;              // set by the launcher of each span kernel
 };
+
+// The decode of a launch with hg heads per workgroup (the host keeps the
+// work items below 2^31 and G dividing H).
+inline void set_decode(KParams& p, int hg) {
+    Decode& d = p.dc;
+    d.ngrp = (p.H + hg - 1) / hg;
+    d.nreal = p.nspan * d.ngrp * p.npg;
+    d.per = (d.nreal + kXcds - 1) / kXcds;
+    d.nchain = p.batch * d.ngrp * p.npg;
+    d.cpx = d.nchain / kXcds;
+    d.by_npg = make_fastdiv((uint32_t)p.npg);
+    d.by_ngrp = make_fastdiv((uint32_t)d.ngrp);
+    d.by_cpx = make_fastdiv((uint32_t)d.cpx);
+    d.by_sps = make_fastdiv((uint32_t)p.sps);
+    d.by_batch = make_fastdiv((uint32_t)p.batch);
+    d.by_hpg = make_fastdiv((uint32_t)(p.G > 0 ? p.H / p.G : 1));
+}
 
 // Backward pass (ssd_bwd_kernels.hip): one workgroup per (chunk, B/C
 // group, subset of hs heads of the group); headdim <= 64.
@@ -125,6 +174,7 @@ struct BParams {
     int32_t nsub, hs;       // head subsets per group, heads per subset
     int32_t reverse;
     float d_init;
+    FastDiv by_nsub, by_G, by_cps, by_npg;  // set by the gradient launcher
 };
 constexpr int kBwdMaxHeads = 64;  // heads one backward workgroup carries at most
 bool bwd_supported(int dtype, int N);

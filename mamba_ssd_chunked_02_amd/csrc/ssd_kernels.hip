@@ -225,8 +225,9 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     constexpr bool SCANL = !is_state(MODE);  // LDS holds the scan buffers
 
     const int hg = is_state(MODE) ? p.hg_state : p.hg_scan;
-    const int ngrp = (p.H + hg - 1) / hg;
-    const int64_t nreal = p.nspan * ngrp * p.npg;
+    const Decode& dc = p.dc;  // this launch's decode (divisions by its sizes)
+    const int ngrp = dc.ngrp;
+    const int64_t nreal = dc.nreal;
     const int tid = threadIdx.x;
     int64_t logical;
     uint32_t epoch = 0;
@@ -259,16 +260,15 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     } else {
         // XCD-aware order: consecutive logical blocks (same span, neighbouring
         // head groups, which share B and C) land on the same XCD and its L2.
-        const int64_t per = (nreal + kXcds - 1) / kXcds;
         const int64_t bid = blk;
-        logical = (bid % kXcds) * per + bid / kXcds;
+        logical = (bid % kXcds) * dc.per + bid / kXcds;
         if (logical >= nreal) return;
     }
     // (the host keeps span x head group x column group below 2^31, so the
     // decode divides in 32 bits)
     int pg, hgi;
     uint32_t span32;
-    const uint32_t nchain = (uint32_t)p.batch * (uint32_t)ngrp * (uint32_t)p.npg;
+    const uint32_t nchain = (uint32_t)dc.nchain;
     if ((MODE == kModeScan || (MODE == kModeState && !p.chunk_out)) && p.fuse_pass == 1 &&
         !p.nseq && nchain % kXcds == 0) {
         // A scan that folds the earlier span states itself, and the state
@@ -282,7 +282,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         // CU and slots n - c .. c - 1 run alone; the alone slots take the
         // first 2c - n ranks, and each shared CU pairs the next heaviest
         // rank with the lightest one left.
-        const uint32_t S = (uint32_t)p.sps, cpx = nchain / kXcds;
+        const uint32_t S = (uint32_t)p.sps, cpx = (uint32_t)dc.cpx;
         const uint32_t x = (uint32_t)(blk % kXcds), slot = (uint32_t)(blk / kXcds);
         const uint32_t n = S * cpx, c = kXcdCus;
         uint32_t rank = slot;
@@ -292,23 +292,23 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
             else if (slot < np) rank = (2 * c - n) + slot;
             else rank = n - 1 - (slot - c);
         }
-        const uint32_t pr = rank / cpx, chain = x * cpx + (rank - pr * cpx);
-        const uint32_t rest = chain / (uint32_t)p.npg;
+        const uint32_t pr = fdiv(rank, dc.by_cpx), chain = x * cpx + (rank - pr * cpx);
+        const uint32_t rest = fdiv(chain, dc.by_npg);
         pg = (int)(chain - rest * (uint32_t)p.npg);
-        const uint32_t seq = rest / (uint32_t)ngrp;
+        const uint32_t seq = fdiv(rest, dc.by_ngrp);
         hgi = (int)(rest - seq * (uint32_t)ngrp);
         span32 = seq * S + (S - 1u - pr);
     } else {
-        const uint32_t lg32 = (uint32_t)logical, rest = lg32 / (uint32_t)p.npg;
+        const uint32_t lg32 = (uint32_t)logical, rest = fdiv(lg32, dc.by_npg);
         pg = (int)(lg32 - rest * (uint32_t)p.npg);
-        span32 = rest / (uint32_t)ngrp;
+        span32 = fdiv(rest, dc.by_ngrp);
         hgi = (int)(rest - span32 * (uint32_t)ngrp);
         if (MODE != kModeFused && !p.nseq && p.batch > 1) {
             // Interleave the sequences' spans, each odd sequence's in reverse
             // order: neighbouring logical spans (one XCD) then pair an early
             // and a late position, the later one first.
             const uint32_t B = (uint32_t)p.batch, S = (uint32_t)p.sps;
-            const uint32_t k = span32 / B, j = span32 % B;
+            const uint32_t k = fdiv(span32, dc.by_batch), j = span32 - k * B;
             const uint32_t sq = 2u * k < S ? B - 1u - j : j;
             span32 = sq * S + ((sq & 1u) ? S - 1u - k : k);
         }
@@ -328,7 +328,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         chunk0 = e.y;
         nck = e.z;
     } else {
-        const uint32_t seq = span32 / (uint32_t)p.sps;
+        const uint32_t seq = fdiv(span32, dc.by_sps);
         const int kin = (int)(span32 - seq * (uint32_t)p.sps);
         start = (int64_t)seq * p.L;
         len = p.L;
@@ -352,7 +352,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
     const int dir = p.reverse ? -1 : 1;
     // token strides (the host keeps them <= 2^24)
     const int XS = (int)p.xs_t, BS = (int)p.bs_t, CS = (int)p.cs_t, DS = (int)p.ds_t;
-    const int grp = (int)((int64_t)h0 * p.G / p.H);
+    const int grp = (int)fdiv((uint32_t)h0, dc.by_hpg);  // h0 G / H
     // Every wave computes, with a valid head even in a quad without one or
     // past the headdim; only active waves store what they computed.
     const int hc = live ? h : h0;
@@ -402,7 +402,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
 
     // span within its sequence, and the sequence (batch mode; varlen never
     // folds or reads these)
-    const uint32_t seq_of = p.sps > 0 ? span32 / (uint32_t)p.sps : span32;
+    const uint32_t seq_of = p.sps > 0 ? fdiv(span32, dc.by_sps) : span32;
     const int kin = (int)(span32 - seq_of * (uint32_t)(p.sps > 0 ? p.sps : 1));
     const bool folds = MODE == kModeFused || (MODE == kModeScan && p.fuse_pass);
     const bool write_final = folds && p.final_state && kin == p.sps - 1;
@@ -1090,8 +1090,10 @@ hipError_t launch_span_hg(const KParams& p, int hg, hipStream_t s) {
     if (nreal == 0) return hipSuccess;
     // the fused kernel takes one ticket per workgroup: exactly nreal of them
     const int64_t grid = MODE == kModeFused ? nreal : (nreal + kXcds - 1) / kXcds * kXcds;
+    KParams q = p;
+    set_decode(q, hg);
     hipLaunchKernelGGL((span_kernel<T, N, HG, MODE>), dim3((unsigned)grid), dim3(kThreads * HG), 0,
-                       s, p);
+                       s, q);
     return hipGetLastError();
 }
 
@@ -1208,8 +1210,11 @@ hipError_t launch_span_state_pair(const KParams& pa, const KParams& pb, int dtyp
     const int64_t n = pa.nspan * pa.H * pa.npg;  // one head per workgroup (both halves)
     if (n == 0) return hipSuccess;
     const int64_t na = (n + kXcds - 1) / kXcds * kXcds;
+    KParams qa = pa, qb = pb;
+    set_decode(qa, 1);
+    set_decode(qb, 1);
 #define SSD_PAIR(T, NN) \
-    hipLaunchKernelGGL((span_state_pair_kernel<T, NN>), dim3((unsigned)(2 * na)), dim3(kThreads), 0, s, pa, pb, na)
+    hipLaunchKernelGGL((span_state_pair_kernel<T, NN>), dim3((unsigned)(2 * na)), dim3(kThreads), 0, s, qa, qb, na)
     if (dtype == 1) {
         switch (N) {
             case 16: SSD_PAIR(bf16, 16); break;
