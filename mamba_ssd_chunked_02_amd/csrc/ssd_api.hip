@@ -569,7 +569,10 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
             if (e != hipSuccess) return SSD_ERR_HIP;
         }
     }
-    if ((mask & SSD_STAGE_STATE) && pl.fuse != 2) {
+    // (plan 1 with one span per sequence: the scan folds no span state, so
+    // the state stage has nothing to form)
+    const bool no_state = pl.fuse == 2 || (pl.fuse == 1 && pl.sps == 1);
+    if ((mask & SSD_STAGE_STATE) && !no_state) {
         if (rev_ws) {
             ssd::KParams pj = p;
             pj.hg_state = 1;

@@ -257,6 +257,20 @@ def test_span_length_invariance(ssd, k):
     check(ssd, q, True, label=f"K={k} varlen rev f32", tuning=tuning)
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_one_span_per_sequence(ssd, reverse):
+    """A batch of short sequences that each fit one span: the scan folds no
+    span state, so no state stage runs and the scan alone writes y and the
+    final state (from init_state); ragged last chunks, both directions."""
+    tuning = {"kernel": "span", "chunks_per_span": 4}
+    p = random_problem(149, 16, 200, 4, 64, 128, dtype="bf16", init_scale=0.5)
+    d = to_dev(p)
+    call = ssd.prepare(d["x"], d["d_raw"], d["d_init"], d["B"], d["C"], init_state=d["init_state"])
+    plan = ssd.ssd_fwd_plan(call.dims, tuning)
+    assert plan.fused_pass == 1 and plan.nspan == 16
+    check(ssd, p, reverse, label=f"one span rev={reverse}", tuning=tuning)
+
+
 @pytest.mark.parametrize("fuse", ["0", "1", "2"])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_state_pass_folded_or_separate(ssd, fuse, reverse):
