@@ -579,9 +579,19 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
             pj.rev_states = rev_ws + pl.off_states;
             pj.rev_decay = (float*)(rev_ws + pl.off_decay);
             e = ssd::launch_span_state_both(pj, d.dtype, d.d_state, s);
+        } else if (pl.hw_npb) {
+            e = ssd::launch_hw_state(p, d.d_state, s);
         } else {
-            e = pl.hw_npb ? ssd::launch_hw_state(p, d.d_state, s)
-                          : ssd::launch_span_state(p, d.dtype, d.d_state, s);
+            // Plan 1 with chains dealt whole to the XCDs: the last span of
+            // each sequence is left out (the scan forms the final state
+            // itself and folds only earlier spans).
+            ssd::KParams ps = p;
+            const int64_t chains = (int64_t)d.batch * ceil_div(d.nheads, pl.hg_state) * pl.npg;
+            if (pl.fuse == 1 && d.nseq == 0 && pl.sps > 1 && chains % ssd::kXcds == 0) {
+                ps.chain_spans = pl.sps - 1;
+                ps.nspan = (int64_t)d.batch * ps.chain_spans;
+            }
+            e = ssd::launch_span_state(ps, d.dtype, d.d_state, s);
         }
         if (e != hipSuccess) return SSD_ERR_HIP;
     }

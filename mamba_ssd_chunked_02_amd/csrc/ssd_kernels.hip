@@ -283,8 +283,9 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         // first 2c - n ranks, and each shared CU pairs the next heaviest
         // rank with the lightest one left.
         const uint32_t S = (uint32_t)p.sps, cpx = (uint32_t)dc.cpx;
+        const uint32_t SL = p.chain_spans ? (uint32_t)p.chain_spans : S;  // spans formed per chain
         const uint32_t x = (uint32_t)(blk % kXcds), slot = (uint32_t)(blk / kXcds);
-        const uint32_t n = S * cpx, c = kXcdCus;
+        const uint32_t n = SL * cpx, c = kXcdCus;
         uint32_t rank = slot;
         if (n > c && n <= 2 * c) {
             const uint32_t np = n - c;  // CUs holding two
@@ -297,7 +298,7 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         pg = (int)(chain - rest * (uint32_t)p.npg);
         const uint32_t seq = fdiv(rest, dc.by_ngrp);
         hgi = (int)(rest - seq * (uint32_t)ngrp);
-        span32 = seq * S + (S - 1u - pr);
+        span32 = seq * S + (SL - 1u - pr);
     } else {
         const uint32_t lg32 = (uint32_t)logical, rest = fdiv(lg32, dc.by_npg);
         pg = (int)(lg32 - rest * (uint32_t)p.npg);
