@@ -181,8 +181,12 @@ int make_plan(const ssd_dims* d, const ssd_tuning* tun, Plan* pl) {
         const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
         if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
     }
-    // The span kernels decode their work items in 32 bits.
+    // The span kernels decode their work items in 32 bits, and the state
+    // pass its threads (four or eight state entries each).
     if (pl->nspan * d->nheads * pl->npg >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
+    const int64_t nstates = d->nseq > 0 ? d->nseq : d->batch;
+    if (nstates * d->nheads * (int64_t)d->headdim * d->d_state >= ((int64_t)1 << 33))
+        return SSD_ERR_SHAPE;
     // The header sits at the start of every plan's workspace; the fused
     // launch's words follow it: one 64-bit ticket/epoch word per chain
     // (sequence, head group, column group), then one flag per workgroup.

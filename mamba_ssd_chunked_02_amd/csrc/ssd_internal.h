@@ -44,6 +44,7 @@ struct Decode {
     int32_t nchain;  // chains: batch x ngrp x npg
     int32_t cpx;     // chains per XCD, nchain / kXcds
     FastDiv by_npg, by_ngrp, by_cpx, by_sps, by_batch, by_hpg;  // hpg = H / G
+    FastDiv by_ev, by_h, by_nb;  // state pass: entry vectors per state, H, N / 16
 };
 
 // Everything the kernels need, passed by value.
@@ -136,6 +137,13 @@ inline void set_decode(KParams& p, int hg) {
     d.by_sps = make_fastdiv((uint32_t)p.sps);
     d.by_batch = make_fastdiv((uint32_t)p.batch);
     d.by_hpg = make_fastdiv((uint32_t)(p.G > 0 ? p.H / p.G : 1));
+}
+
+// The decode of a state pass moving V state entries per thread.
+inline void set_pass_decode(KParams& p, int V) {
+    p.dc.by_ev = make_fastdiv((uint32_t)((int64_t)p.P * p.N / V));
+    p.dc.by_h = make_fastdiv((uint32_t)p.H);
+    p.dc.by_nb = make_fastdiv((uint32_t)(p.N / 16));
 }
 
 // Backward pass (ssd_bwd_kernels.hip): one workgroup per (chunk, B/C

@@ -919,9 +919,12 @@ __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     const int EV = p.P * N / V;
     const int64_t S = p.nseq ? p.nseq : p.batch;
     if (gid >= S * p.H * EV) return;
-    const int ev = (int)(gid % EV);
-    const int h = (int)((gid / EV) % p.H);
-    const int64_t i = gid / EV / p.H;
+    // (divisions as multiply-highs set by the launcher: threads < 2^31)
+    const uint32_t g32 = (uint32_t)gid, r1 = fdiv(g32, p.dc.by_ev);
+    const int ev = (int)(g32 - r1 * (uint32_t)EV);
+    const uint32_t i32 = fdiv(r1, p.dc.by_h);
+    const int h = (int)(r1 - i32 * (uint32_t)p.H);
+    const int64_t i = i32;
     int64_t s0, s1;
     if (p.nseq) {
         s0 = p.span_off[i];
@@ -935,8 +938,9 @@ __device__ __forceinline__ void state_pass_body(const KParams& p, int64_t gid) {
     for (int j = 0; j < V; ++j) {
         const int o = ev * V + j;
         const int lane = (o >> 2) & 63, q = o >> 8;
-        const int n = 16 * (q % NB) + 4 * (lane >> 4) + (o & 3);
-        const int pp = 16 * (q / NB) + (lane & 15);
+        const int qb = (int)fdiv((uint32_t)q, p.dc.by_nb);  // q / NB
+        const int n = 16 * (q - qb * NB) + 4 * (lane >> 4) + (o & 3);
+        const int pp = 16 * qb + (lane & 15);
         idx[j] = n * p.P + pp;
     }
     const int64_t hb = (i * p.H + h) * (int64_t)N * p.P;
@@ -1243,10 +1247,13 @@ hipError_t launch_state_pass_pair(const KParams& pa, const KParams& pb, int dtyp
     const int64_t n = S * pa.H * (int64_t)pa.P * pa.N / V;
     if (n == 0) return hipSuccess;
     const int64_t na = (n + 255) / 256;
+    KParams qa = pa, qb = pb;
+    set_pass_decode(qa, V);
+    set_pass_decode(qb, V);
     if (dtype == 1)
-        hipLaunchKernelGGL(state_pass_pair_kernel<bf16>, dim3((unsigned)(2 * na)), dim3(256), 0, s, pa, pb, na);
+        hipLaunchKernelGGL(state_pass_pair_kernel<bf16>, dim3((unsigned)(2 * na)), dim3(256), 0, s, qa, qb, na);
     else
-        hipLaunchKernelGGL(state_pass_pair_kernel<float>, dim3((unsigned)(2 * na)), dim3(256), 0, s, pa, pb, na);
+        hipLaunchKernelGGL(state_pass_pair_kernel<float>, dim3((unsigned)(2 * na)), dim3(256), 0, s, qa, qb, na);
     return hipGetLastError();
 }
 
@@ -1257,10 +1264,12 @@ hipError_t launch_state_pass(const KParams& p, int dtype, hipStream_t s) {
     const int64_t n = S * p.H * (int64_t)p.P * p.N / V;
     if (n == 0) return hipSuccess;
     const dim3 grid((unsigned)((n + 255) / 256));
+    KParams q = p;
+    set_pass_decode(q, V);
     if (s16)
-        hipLaunchKernelGGL(state_pass_kernel<bf16>, grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(state_pass_kernel<bf16>, grid, dim3(256), 0, s, q);
     else
-        hipLaunchKernelGGL(state_pass_kernel<float>, grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(state_pass_kernel<float>, grid, dim3(256), 0, s, q);
     return hipGetLastError();
 }
 

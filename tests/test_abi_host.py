@@ -69,6 +69,10 @@ def test_workspace_bytes(m):
     assert m.ssd_fwd_workspace_bytes(m.make_dims(1, 64, 2, 16, 16, chunk_size=32)) == 0
     assert m.ssd_fwd_workspace_bytes(m.make_dims(1, 64, 2, 24, 16)) == 0
     assert m.ssd_fwd_workspace_bytes(m.make_dims(2, 64, 2, 16, 16, nseq=3)) == 0
+    # sequences x heads x state entries: 2^33 and more are out of range (the
+    # state pass decodes its threads in 32 bits), just below is accepted
+    assert m.ssd_fwd_workspace_bytes(m.make_dims(1 << 12, 64, 64, 256, 128)) == 0
+    assert m.ssd_fwd_workspace_bytes(m.make_dims((1 << 12) - 1, 64, 64, 256, 128)) > 0
 
 
 FAKE = 1 << 20  # 16-byte aligned, never dereferenced: every call below is rejected
