@@ -181,6 +181,14 @@ int make_plan(const ssd_dims* d, const ssd_tuning* tun, Plan* pl) {
         const int64_t work = pl->nspan * ceil_div(d->nheads, pl->hg_scan) * pl->npg;
         if (pl->fuse == 2 && work >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
     }
+    // Span kernels: two heads per state workgroup (they share its B tile)
+    // where that still leaves at least 128 state workgroups; with fewer,
+    // one-head walks finish sooner (2 x 2048 tokens x 24 heads: 26.3 vs 26.6
+    // us per step; 8192 tokens x 80 heads: 112.6 vs 113.7; 256 tokens x 2
+    // heads: 11.0 vs 10.5).
+    if (!hw && !t.heads_state && hpg % 2 == 0 && hs_max >= 2 &&
+        pl->nspan * ceil_div(d->nheads, 2) * pl->npg >= 128)
+        pl->hg_state = 2;
     // The span kernels decode their work items in 32 bits, and the state
     // pass its threads (four or eight state entries each).
     if (pl->nspan * d->nheads * pl->npg >= ((int64_t)1 << 31)) return SSD_ERR_SHAPE;
