@@ -587,7 +587,7 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
     if ((mask & SSD_STAGE_STATE) && !no_state) {
         if (rev_ws) {
             ssd::KParams pj = p;
-            pj.hg_state = 1;
+            pj.hg_state = d.dtype == SSD_BF16 && (d.nheads / d.ngroups) % 2 == 0 ? 2 : 1;
             pj.rev_states = rev_ws + pl.off_states;
             pj.rev_decay = (float*)(rev_ws + pl.off_decay);
             e = ssd::launch_span_state_both(pj, d.dtype, d.d_state, s);

@@ -1192,8 +1192,15 @@ hipError_t launch_span_scan(const KParams& p, int dtype, int N, hipStream_t s) {
 // Both directions' span states in one walk (one head per workgroup; batch
 // mode, whole spans).
 hipError_t launch_span_state_both(const KParams& p, int dtype, int N, hipStream_t s) {
-    if (p.hg_state != 1 || p.nseq) return hipErrorInvalidValue;
-    if (dtype == 1) {
+    if ((p.hg_state != 1 && !(p.hg_state == 2 && dtype == 1)) || p.nseq) return hipErrorInvalidValue;
+    if (dtype == 1 && p.hg_state == 2) {
+        switch (N) {
+            case 16: return launch_span_hg<bf16, 16, 2, kModeStateBoth>(p, 2, s);
+            case 32: return launch_span_hg<bf16, 32, 2, kModeStateBoth>(p, 2, s);
+            case 64: return launch_span_hg<bf16, 64, 2, kModeStateBoth>(p, 2, s);
+            case 128: return launch_span_hg<bf16, 128, 2, kModeStateBoth>(p, 2, s);
+        }
+    } else if (dtype == 1) {
         switch (N) {
             case 16: return launch_span_hg<bf16, 16, 1, kModeStateBoth>(p, 1, s);
             case 32: return launch_span_hg<bf16, 32, 1, kModeStateBoth>(p, 1, s);
