@@ -62,16 +62,18 @@ int32_t choose_k(int64_t nch, int64_t groups, int64_t cps) {
 // spans to pay for the state pass, so the planner takes them for problems
 // with at least 16384 chunk-head-column-group work items (on one MI355X the
 // span kernels are faster below that: 119 vs 146 us on 8192 tokens x 80
-// heads).  Spans: the longest of 32, 16, ... chunks that still give >= 2048
-// waves; 4 heads per workgroup at d_state 128 (they share the B / C tiles
-// and the causal C B^T), 2 at d_state 64.
+// heads).  Spans: 64 chunks where that still gives >= 8192 waves (1M tokens
+// x 8 heads x 192: 4.62 vs 4.73 ms per bidirectional step with 32), else the
+// longest of 32, 16, ... chunks that still give >= 2048 waves; 4 heads per
+// workgroup at d_state 128 (they share the B / C tiles and the causal
+// C B^T), 2 at d_state 64.
 bool choose_hw(const ssd_tuning& t, int64_t nch, int64_t heads, int64_t npg, int32_t hpg,
                int32_t N, int32_t* K, int32_t* npb, int32_t* hg) {
     if (t.kernel == 1) return false;
     if (t.kernel != 2 && nch * heads * npg < 16384) return false;
     int32_t b = t.cols_per_wave ? t.cols_per_wave / 16 : 2;
     auto waves = [&](int32_t k) { return ceil_div(nch, k) * heads * npg * (4 / b); };
-    int32_t k = 32;
+    int32_t k = waves(64) >= 8192 ? 64 : 32;
     while (k > 1 && waves(k) < 2048) k /= 2;
     int32_t g = N >= 128 ? 4 : 2;
     while (hpg % g) g /= 2;

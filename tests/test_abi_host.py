@@ -328,7 +328,7 @@ def test_plan_head_wave_kernels(m):
     assert (varlen.head_wave, varlen.chunks_per_span, varlen.cols_per_wave, varlen.heads_per_wg,
             varlen.heads_per_state_wg, varlen.fused_pass) == (1, 16, 32, 4, 2, 0)
     bidir = m.ssd_fwd_plan(m.make_dims(1, 1 << 20, 8, 192, 64))
-    assert (bidir.head_wave, bidir.chunks_per_span, bidir.cols_per_wave, bidir.heads_per_wg) == (1, 32, 32, 2)
+    assert (bidir.head_wave, bidir.chunks_per_span, bidir.cols_per_wave, bidir.heads_per_wg) == (1, 64, 32, 2)
     wide = m.ssd_fwd_plan(m.make_dims(1, 8192, 80, 64, 128))   # 10240 items: span kernels
     assert (wide.head_wave, wide.chunks_per_span, wide.fused_pass) == (0, 8, 0)
     assert m.ssd_fwd_plan(m.make_dims(2, 2048, 24, 64, 128)).head_wave == 0   # layer: span kernels
@@ -428,7 +428,7 @@ def test_noalloc_rejects_sizes_past_its_scratch(m):
     64 MiB array with SSD_ERR_SCRATCH, before any HIP call (NULL pointers:
     nothing could be launched even if the check were missing)."""
     assert m.ssd_fwd_noalloc_max_bytes() == 64 << 20
-    big = m.make_dims(1, 1 << 20, 8, 192, 64)
+    big = m.make_dims(4, 1 << 20, 8, 192, 64)
     assert m.ssd_fwd_workspace_bytes(big) > 64 << 20
     lay = m.SsdLayout(8 * 192, 192, 8, 1, 64, 64, 64, 64, 8 * 192, 192, 8 * 192, 192)
     rc = m.library().ssd_fwd_noalloc(ctypes.byref(big), ctypes.byref(lay), None, None, -4.6,
