@@ -93,8 +93,11 @@ def stage_bytes(w, plan, spans_used: int) -> dict:
     shared by the H/G heads of a group), y (P*e).  Per span-head: one N x P
     state stored in the input type (plus a 4-byte fp32 decay); init and
     final states are fp32.  e = element size of the inputs.
-    fused_pass 1: span_scan is charged each span state and decay once, plus
-    init and final states, and there is no pass.  fused_pass 2: the one
+    fused_pass 1: the state launch forms only the first sps - 1 spans of
+    each sequence (no scan reads the last one's state) and is charged their
+    tokens' inputs and their states; span_scan is charged those span states
+    and decays once, plus init and final states, and there is no pass.
+    fused_pass 2: the one
     launch is charged its inputs and outputs plus each span state it hands
     on (all but the last span of a sequence) written once; the reads of
     those states by later spans are not counted."""
@@ -113,8 +116,11 @@ def stage_bytes(w, plan, spans_used: int) -> dict:
         handed = (spans_used - S) * H
         return {"fused": x + draw + 2 * bc + y + init + fin + handed * (N * P * e + 4)}
     if plan.fused_pass == 1:
-        return {"state": x + draw + bc + st + dec,
-                "scan": x + draw + 2 * bc + st + dec + init + fin + y}
+        formed = spans_used - S                    # batch mode: all but each last span
+        frac = formed * 64 * plan.chunks_per_span / T if T else 0.0
+        stf, decf = formed * H * N * P * e, formed * H * 4
+        return {"state": round((x + draw + bc) * frac) + stf + decf,
+                "scan": x + draw + 2 * bc + stf + decf + init + fin + y}
     return {
         "state": x + draw + bc + st + dec,
         "pass": 2 * st + dec + fin + init,
@@ -130,7 +136,10 @@ def stage_flops(w, plan, spans_used: int) -> dict:
     inter-chunk term C Hprev, 2NP; the causal intra-chunk product, (Q+1)P on
     average over a chunk's 64 positions.  Per token and B/C group: the
     causal C B^T, (Q+1)N.  Per span-head: the pair combine, 2NP.  Recomputing
-    a state inside span_scan is not counted."""
+    a state inside span_scan is not counted.  fused_pass 1: the state launch
+    forms the first sps - 1 spans of each sequence (their tokens' chunk
+    states and one combine per span); the scan carries the last span's
+    chunk states on to the final state."""
     T, H, P, N, G, Q = w.tokens, w.nheads, w.headdim, w.d_state, w.ngroups, 64
     state = 2 * N * P * T * H
     scan = (2 * N * P + (Q + 1) * P) * T * H + (Q + 1) * N * T * G
@@ -138,7 +147,9 @@ def stage_flops(w, plan, spans_used: int) -> dict:
     if plan.fused_pass == 2:
         return {"fused": state + scan + combine}
     if plan.fused_pass == 1:
-        return {"state": state, "scan": scan + combine}
+        formed = spans_used - w.nstates
+        fstate = 2 * N * P * formed * 64 * plan.chunks_per_span * H
+        return {"state": fstate, "scan": scan + (state - fstate) + 2 * N * P * formed * H}
     return {"state": state, "pass": combine, "scan": scan}
 
 
@@ -334,10 +345,12 @@ def workload_line(m, name: str, dev, with_bwd: bool) -> dict:
     scalls = step_calls(m, w, d, calls, ycat)
     plan = m.ssd_fwd_plan(calls[0].dims)
     big = w.tokens >= (1 << 20)
-    steps, warm = (3, 1) if big else (20, 3)
+    # enough warm-up and steps that first-call costs do not show (a step of
+    # the largest workload takes ~5 ms)
+    steps, warm = (20, 5) if big else (200, 20)
     fwd = wall_ms(lambda: [c.run() for c in scalls], steps, warm)
     stages = plan_stages(m, w, plan)
-    us = stage_times_us(m, calls, stages, 2 if big else 10)
+    us = stage_times_us(m, calls, stages, 5 if big else 50)
     used = spans_used(w, plan, d["cu_seqlens"])
     by = stage_bytes(w, plan, used)
     dom = max((n for n in us if n in by), key=lambda n: us[n])
@@ -356,7 +369,7 @@ def workload_line(m, name: str, dev, with_bwd: bool) -> dict:
     if with_bwd:
         bcalls = backward_calls(m, w, d, dev, calls, ycat)
         if bcalls:
-            bsteps, bwarm = (2, 1) if big else (10, 2)
+            bsteps, bwarm = (5, 2) if big else (50, 5)
             bwd = wall_ms(lambda: [bc.run() for bc in bcalls], bsteps, bwarm)
             line["bwd_ms_per_step"] = round(bwd, 5)
             line["bwd_mtokens_per_s"] = round(w.tokens / (bwd * 1e-3) / 1e6, 3)

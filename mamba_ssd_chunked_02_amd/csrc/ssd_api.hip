@@ -601,12 +601,10 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
         } else if (pl.hw_npb) {
             e = ssd::launch_hw_state(p, d.d_state, s);
         } else {
-            // Plan 1 with chains dealt whole to the XCDs: the last span of
-            // each sequence is left out (the scan forms the final state
-            // itself and folds only earlier spans).
+            // Plan 1: the last span of each sequence is left out (the scan
+            // forms the final state itself and folds only earlier spans).
             ssd::KParams ps = p;
-            const int64_t chains = (int64_t)d.batch * ceil_div(d.nheads, pl.hg_state) * pl.npg;
-            if (pl.fuse == 1 && d.nseq == 0 && pl.sps > 1 && chains % ssd::kXcds == 0) {
+            if (pl.fuse == 1 && d.nseq == 0 && pl.sps > 1) {
                 ps.chain_spans = pl.sps - 1;
                 ps.nspan = (int64_t)d.batch * ps.chain_spans;
             }

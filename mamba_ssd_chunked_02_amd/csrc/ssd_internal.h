@@ -114,10 +114,9 @@ struct KParams {
     float* rev_decay;       // ... and span decays, same layout as states / decay
     int32_t state_f32;      // span states stored in float32 whatever the input
                             // type (span kernels, plans 0 and 1)
-    int32_t chain_spans;    // (state launch of plan 1, chains dealt whole to the
-                            // XCDs) spans per sequence it forms: the first
-                            // sps - 1 (no scan folds the last one's state);
-                            // 0 = all
+    int32_t chain_spans;    // (state launch of plan 1, batch mode) spans per
+                            // sequence it forms: the first sps - 1 (no scan
+                            // folds the last one's state); 0 = all
     float d_init;
     Decode dc;              // set by the launcher of each span kernel
 };

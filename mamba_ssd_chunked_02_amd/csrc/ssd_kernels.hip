@@ -307,11 +307,14 @@ __device__ __forceinline__ void span_body(const KParams& p, int64_t blk,
         if (MODE != kModeFused && !p.nseq && p.batch > 1) {
             // Interleave the sequences' spans, each odd sequence's in reverse
             // order: neighbouring logical spans (one XCD) then pair an early
-            // and a late position, the later one first.
+            // and a late position, the later one first.  (A launch forming
+            // only the first chain_spans spans of each sequence interleaves
+            // those; with batch 1 its work items are those spans already.)
             const uint32_t B = (uint32_t)p.batch, S = (uint32_t)p.sps;
+            const uint32_t SL = p.chain_spans ? (uint32_t)p.chain_spans : S;
             const uint32_t k = fdiv(span32, dc.by_batch), j = span32 - k * B;
-            const uint32_t sq = 2u * k < S ? B - 1u - j : j;
-            span32 = sq * S + ((sq & 1u) ? S - 1u - k : k);
+            const uint32_t sq = 2u * k < SL ? B - 1u - j : j;
+            span32 = sq * S + ((sq & 1u) ? SL - 1u - k : k);
         }
     }
     const int64_t span = span32;
