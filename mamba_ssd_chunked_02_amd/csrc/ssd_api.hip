@@ -490,8 +490,7 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
                     const ssd_layout* layout, const void* x, const void* d_raw, float d_init,
                     const void* B, const void* C, const float* init_state,
                     const int32_t* cu_seqlens, int32_t reverse, void* y, float* final_state,
-                    void* workspace, size_t workspace_bytes, void* stream, char* rev_ws,
-                    ssd::KParams* params_out = nullptr) {
+                    void* workspace, size_t workspace_bytes, void* stream, char* rev_ws) {
     if (mask & ~(uint32_t)SSD_STAGE_ALL) return SSD_ERR_SHAPE;
     Plan pl;
     const int st = make_plan(dims, tuning, &pl);
@@ -571,10 +570,6 @@ static int fwd_impl(uint32_t mask, const ssd_dims* dims, const ssd_tuning* tunin
     p.state_f32 = pl.state_f32;
     p.sync = (uint32_t*)(ws + pl.off_sync);
     p.d_init = d_init;
-    if (params_out) {  // (batch mode) the checked launch parameters, nothing launched
-        *params_out = p;
-        return SSD_OK;
-    }
 
     hipError_t e = hipSuccess;
     if (d.nseq > 0) {
@@ -675,23 +670,6 @@ int ssd_fwd_bidir(const ssd_dims* dims, const ssd_tuning* tuning, const ssd_layo
         const int c = fwd_impl(SSD_STAGE_STATE, dims, tuning, layout, x, d_raw, d_init, B, C, init_fwd,
                                nullptr, 0, y_fwd, final_fwd, wf, half, stream, wr);
         if (c != SSD_OK) return c;
-    }
-    if (joint && pl.hw_npb) {
-        // head-wave plan: both directions' state passes in one launch, then
-        // both scans in one (the second direction's workgroups fill the
-        // first's tail)
-        ssd::KParams pd[2];
-        for (int r = 0; r < 2; ++r) {
-            const int c = fwd_impl(0, dims, tuning, layout, x, d_raw, d_init, B, C,
-                                   r ? init_rev : init_fwd, nullptr, r, r ? y_rev : y_fwd,
-                                   r ? final_rev : final_fwd, r ? wr : wf, half, stream, nullptr, &pd[r]);
-            if (c != SSD_OK) return c;
-        }
-        if (pd[0].fuse_pass || pd[1].fuse_pass) return SSD_ERR_HIP;  // head-wave plans keep the pass
-        hipStream_t s = (hipStream_t)stream;
-        if (ssd::launch_state_pass_pair(pd[0], pd[1], d.dtype, s) != hipSuccess) return SSD_ERR_HIP;
-        if (ssd::launch_hw_scan_pair(pd[0], pd[1], d.d_state, s) != hipSuccess) return SSD_ERR_HIP;
-        return SSD_OK;
     }
     for (int r = 0; r < 2; ++r) {
         const int c = ssd_fwd_ex(rest, dims, tuning, layout, x, d_raw, d_init, B, C,

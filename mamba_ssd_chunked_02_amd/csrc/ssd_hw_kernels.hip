@@ -225,13 +225,16 @@ constexpr int hw_occupancy() {
     return (HG == 4 || (N == 64 && HG == 2)) ? 2 : 1;
 }
 
-// Head-wave span workgroup number bid of the launch p; see the file comment.
+// Head-wave span kernel; see the file comment.
 template <int N, int HG, int NPB, int MODE>
-__device__ __forceinline__ void hw_span_body(const KParams& p, int64_t bid,
-                                             HwSmem<N, HG, NPB, MODE == kHwScan>& sm) {
+__global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE>())) void hw_span_kernel(
+    KParams p) {
     using Cf = HwCfg<N, HG, NPB>;
+    using Sm = HwSmem<N, HG, NPB, MODE == kHwScan>;
     constexpr int NB = Cf::NB, KN = Cf::KN, WPH = Cf::WPH, NW = Cf::NW;
     constexpr bool SCAN = MODE == kHwScan;
+    __shared__ Sm sm;
+    touch_args(p);
 
     // XCD-aware order: consecutive logical blocks (same span, neighbouring
     // head groups, which share B and C) land on the same XCD and its L2.
@@ -239,6 +242,7 @@ __device__ __forceinline__ void hw_span_body(const KParams& p, int64_t bid,
     // work items stay below 2^31)
     const Decode& dc = p.dc;
     const int ngrp = dc.ngrp;  // H / HG
+    const int64_t bid = blockIdx.x;
     const int64_t logical = (bid % kXcds) * dc.per + bid / kXcds;
     if (logical >= dc.nreal) return;
     const uint32_t lg32 = (uint32_t)logical, rest = fdiv(lg32, dc.by_npg);
@@ -585,44 +589,6 @@ __device__ __forceinline__ void hw_span_body(const KParams& p, int64_t bid,
 }
 
 template <int N, int HG, int NPB, int MODE>
-__global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE>())) void hw_span_kernel(
-    KParams p) {
-    __shared__ HwSmem<N, HG, NPB, MODE == kHwScan> sm;
-    touch_args(p);
-    hw_span_body<N, HG, NPB, MODE>(p, blockIdx.x, sm);
-}
-
-// Two launches' workgroups in one grid (the two directions' scans of a
-// bidirectional call): workgroups below na run pa's, the rest pb's; na is a
-// multiple of the XCD count, so each half keeps its XCD-aware order, and the
-// second half's workgroups start while the first half's last ones finish.
-template <int N, int HG, int NPB, int MODE>
-__global__ __launch_bounds__(64 * HG * (4 / NPB), (hw_occupancy<N, HG, NPB, MODE>())) void hw_span_pair_kernel(
-    KParams pa, KParams pb, int64_t na) {
-    __shared__ HwSmem<N, HG, NPB, MODE == kHwScan> sm;
-    if ((int64_t)blockIdx.x < na) {
-        touch_args(pa);
-        hw_span_body<N, HG, NPB, MODE>(pa, blockIdx.x, sm);
-    } else {
-        touch_args(pb);
-        hw_span_body<N, HG, NPB, MODE>(pb, (int64_t)blockIdx.x - na, sm);
-    }
-}
-
-template <int N, int HG, int NPB, int MODE>
-hipError_t launch_hw_pair_t(const KParams& pa, const KParams& pb, hipStream_t s) {
-    const int64_t nreal = pa.nspan * (pa.H / HG) * pa.npg;
-    if (nreal == 0) return hipSuccess;
-    const int64_t na = (nreal + kXcds - 1) / kXcds * kXcds;
-    KParams qa = pa, qb = pb;
-    set_decode(qa, HG);
-    set_decode(qb, HG);
-    hipLaunchKernelGGL((hw_span_pair_kernel<N, HG, NPB, MODE>), dim3((unsigned)(2 * na)),
-                       dim3(HwCfg<N, HG, NPB>::TH), 0, s, qa, qb, na);
-    return hipGetLastError();
-}
-
-template <int N, int HG, int NPB, int MODE>
 hipError_t launch_hw_t(const KParams& p, hipStream_t s) {
     const int64_t nreal = p.nspan * (p.H / HG) * p.npg;
     if (nreal == 0) return hipSuccess;
@@ -649,24 +615,6 @@ hipError_t launch_hw_n(const KParams& p, hipStream_t s) {
             case 14: return launch_hw_t<N, 1, 4, MODE>(p, s);
             case 24: return launch_hw_t<N, 2, 4, MODE>(p, s);
             case 44: return launch_hw_t<N, 4, 4, MODE>(p, s);
-        }
-    }
-    return hipErrorInvalidValue;
-}
-
-// Both directions' scans in one launch (same sizes and plan).
-template <int N>
-hipError_t launch_hw_scan_pair_n(const KParams& pa, const KParams& pb, hipStream_t s) {
-    switch (pa.hg_scan * 10 + pa.hw_npb) {
-        case 12: return launch_hw_pair_t<N, 1, 2, kHwScan>(pa, pb, s);
-        case 22: return launch_hw_pair_t<N, 2, 2, kHwScan>(pa, pb, s);
-        case 42: return launch_hw_pair_t<N, 4, 2, kHwScan>(pa, pb, s);
-    }
-    if constexpr (N <= 64) {
-        switch (pa.hg_scan * 10 + pa.hw_npb) {
-            case 14: return launch_hw_pair_t<N, 1, 4, kHwScan>(pa, pb, s);
-            case 24: return launch_hw_pair_t<N, 2, 4, kHwScan>(pa, pb, s);
-            case 44: return launch_hw_pair_t<N, 4, 4, kHwScan>(pa, pb, s);
         }
     }
     return hipErrorInvalidValue;
@@ -710,13 +658,5 @@ size_t hw_lds_bytes(int N, int hg, int npb, bool scan) {
 
 hipError_t launch_hw_state(const KParams& p, int N, hipStream_t s) { return launch_hw<kHwState>(p, N, s); }
 hipError_t launch_hw_scan(const KParams& p, int N, hipStream_t s) { return launch_hw<kHwScan>(p, N, s); }
-hipError_t launch_hw_scan_pair(const KParams& pa, const KParams& pb, int N, hipStream_t s) {
-    if (pa.hg_scan != pb.hg_scan || pa.hw_npb != pb.hw_npb || pa.nspan != pb.nspan) return hipErrorInvalidValue;
-    switch (N) {
-        case 64: return launch_hw_scan_pair_n<64>(pa, pb, s);
-        case 128: return launch_hw_scan_pair_n<128>(pa, pb, s);
-    }
-    return hipErrorInvalidValue;
-}
 
 }  // namespace ssd

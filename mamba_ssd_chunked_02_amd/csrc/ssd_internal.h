@@ -232,7 +232,6 @@ bool hw_supported(int dtype, int N, int hg, int npb);
 size_t hw_lds_bytes(int N, int hg, int npb, bool scan);
 hipError_t launch_hw_state(const KParams& p, int N, hipStream_t s);
 hipError_t launch_hw_scan(const KParams& p, int N, hipStream_t s);
-hipError_t launch_hw_scan_pair(const KParams& pa, const KParams& pb, int N, hipStream_t s);
 
 // Most heads one span workgroup can carry for this d_state.
 int span_max_heads(int dtype, int N, bool scan);
