@@ -276,6 +276,15 @@ def backward_calls(m, w, d, dev, calls, ycat):
     return out
 
 
+def warm_for(fn, seconds: float) -> None:
+    """Call fn until `seconds` of wall time have passed."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
 def wall_ms(fn, steps: int, warmup: int) -> float:
     """Wall-clock ms per call of fn: warmup calls, then steps calls between
     two synchronizations."""
@@ -346,8 +355,11 @@ def workload_line(m, name: str, dev, with_bwd: bool) -> dict:
     plan = m.ssd_fwd_plan(calls[0].dims)
     big = w.tokens >= (1 << 20)
     # enough warm-up and steps that first-call costs do not show (a step of
-    # the largest workload takes ~5 ms)
+    # the largest workload takes ~5 ms); the warm-up also lasts at least
+    # 0.2 s, so a GPU that sat idle (the CPU baseline runs before these
+    # lines) is back at its working clock
     steps, warm = (20, 5) if big else (200, 20)
+    warm_for(lambda: [c.run() for c in scalls], 0.2)
     fwd = wall_ms(lambda: [c.run() for c in scalls], steps, warm)
     stages = plan_stages(m, w, plan)
     us = stage_times_us(m, calls, stages, 5 if big else 50)
