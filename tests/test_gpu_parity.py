@@ -413,6 +413,7 @@ BIDIR_JOINT = [
     (1, 512, 2, 64, 32, "f32", {"kernel": "span", "chunks_per_span": 8, "state_pass": "fold"}),
     (3, 384, 2, 16, 32, "bf16", {"kernel": "span", "chunks_per_span": 2, "state_pass": "pass"}),
     (2, 512, 2, 64, 128, "bf16", {"kernel": "span", "chunks_per_span": 4, "state_f32": 1}),  # fp32 span states
+    (2, 256, 2, 64, 128, "bf16", {"kernel": "span", "chunks_per_span": 4}),  # one span each: no state stage
 ]
 
 
